@@ -1,0 +1,248 @@
+/*
+ * CPU oracle for MoE token layout, dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg load this library; the HIP product path
+ * never calls it, and the two share no code, headers or constants.
+ *
+ * It is the plain definition of what the hot path computes, written as
+ * single-threaded loops in the pages' order, with no blocking or fusion.
+ *
+ * Pages cited (by title):
+ *   [SYM] "DeepEP Symmetric Memory 全面架构分析"
+ *         (DeepEP symmetric memory: full architecture analysis)
+ *   [V2]  "DeepEP V2 ElasticBuffer 架构深度分析"
+ *         (DeepEP V2 ElasticBuffer architecture in depth; it has no section
+ *         headings, so its code blocks are cited by what they show)
+ *   [V1]  "第 3 章 V1：Buffer 初始化与通信域建立"
+ *         (chapter 3, V1 buffer initialisation and communicator set-up)
+ *
+ * Notation: T tokens, H hidden (bf16 elements per row), E experts, K top-k,
+ * R destination ranks, L = E/R local experts per rank, G scale-out groups,
+ * A expert alignment, S rows per rank slice.  rank(e) = e / L.
+ *
+ * Error statuses (the oracle's own numbering):
+ *   ORACLE_OK           0
+ *   ORACLE_CAPACITY    -3   some rank's aligned rows exceed S
+ *   ORACLE_BAD_EXPERT  -4   an id outside [0,E) other than -1; reported in
+ *                           preference to a capacity overflow
+ * An id of -1 marks an empty top-k entry and is not an error.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_CAPACITY (-3)
+#define ORACLE_BAD_EXPERT (-4)
+
+static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+static int valid_expert(int32_t e, int32_t E) { return e >= 0 && e < E; }
+
+/*
+ * Routing layout for one source rank.
+ *
+ * [SYM] §6.1 lists what dispatch derives from topk_idx: per-scale-up-rank and
+ * per-expert prefix sums, the unaligned per-expert receive counts, the
+ * expert_alignment, and a destination buffer slot per (token, top-k) entry.
+ * [SYM] §7.3 reads back, per scale-up rank, the received token count and, per
+ * local expert, a count whose sum is the expanded (token, expert) row count.
+ * [V1] §3.2 groups ranks by eight (rdma_rank = rank / 8); with G groups the
+ * group of rank r is r / (R/G).
+ *
+ * Outputs (all caller-allocated):
+ *   expert_count[E]      rows routed to each expert (unaligned count)
+ *   expert_offset[E]     first row of expert e's segment inside its rank's
+ *                        slice: the sum of align_up(count, A) over the lower
+ *                        local experts of the same rank
+ *   rank_row_count[R]    expanded rows per rank (sum of its experts' counts)
+ *   rank_token_count[R]  tokens with at least one entry on the rank
+ *   group_token_count[G] tokens with at least one entry in the group (NULL ok)
+ *   is_token_in_rank[T*R] 1 if the token has an entry on the rank, else 0
+ *   token_slot[T*K]      rank(e)*S + expert_offset[e] + pos, where pos counts
+ *                        the earlier entries (token-major, then top-k order)
+ *                        that name the same expert; -1 for empty or bad ids
+ *                        and for rows at or beyond S inside their slice
+ */
+int oracle_layout(int32_t T, int32_t K, int32_t E, int32_t R, int32_t G, int32_t A,
+                  int64_t S, const int32_t *topk_idx, int32_t *expert_count,
+                  int32_t *expert_offset, int32_t *rank_row_count,
+                  int32_t *rank_token_count, int32_t *group_token_count,
+                  uint8_t *is_token_in_rank, int32_t *token_slot)
+{
+    const int32_t L = E / R;
+    const int32_t ranks_per_group = R / G;
+    int bad = 0, over = 0;
+
+    /* expert histogram */
+    for (int32_t e = 0; e < E; ++e) expert_count[e] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < K; ++j) {
+            int32_t e = topk_idx[t * K + j];
+            if (e == -1) continue;
+            if (!valid_expert(e, E)) { bad = 1; continue; }
+            expert_count[e] += 1;
+        }
+    }
+
+    /* per-rank rows and within-slice expert offsets (exclusive scan over the
+     * rank's local experts of the aligned counts) */
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t run = 0, rows = 0;
+        for (int32_t l = 0; l < L; ++l) {
+            int32_t e = r * L + l;
+            expert_offset[e] = (int32_t)run;
+            run += align_up(expert_count[e], A);
+            rows += expert_count[e];
+        }
+        rank_row_count[r] = (int32_t)rows;
+        if (run > S) over = 1;
+    }
+
+    /* token-to-rank map and unique-token counts per rank and per group */
+    for (int32_t r = 0; r < R; ++r) rank_token_count[r] = 0;
+    if (group_token_count)
+        for (int32_t g = 0; g < G; ++g) group_token_count[g] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t r = 0; r < R; ++r) {
+            uint8_t in = 0;
+            for (int32_t j = 0; j < K; ++j) {
+                int32_t e = topk_idx[t * K + j];
+                if (valid_expert(e, E) && e / L == r) in = 1;
+            }
+            is_token_in_rank[t * R + r] = in;
+            rank_token_count[r] += in;
+        }
+        if (group_token_count) {
+            for (int32_t g = 0; g < G; ++g) {
+                int in = 0;
+                for (int32_t r = g * ranks_per_group; r < (g + 1) * ranks_per_group; ++r)
+                    if (is_token_in_rank[t * R + r]) in = 1;
+                group_token_count[g] += in;
+            }
+        }
+    }
+
+    /* slots: a counting sort over the (token, top-k) entries in token-major
+     * order, so each expert segment holds its rows in ascending source token
+     * (then ascending top-k position) */
+    int64_t *cursor = (int64_t *)calloc((size_t)(E > 0 ? E : 1), sizeof(int64_t));
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < K; ++j) {
+            int32_t e = topk_idx[t * K + j];
+            if (!valid_expert(e, E)) { token_slot[t * K + j] = -1; continue; }
+            int64_t off = expert_offset[e] + cursor[e];
+            cursor[e] += 1;
+            token_slot[t * K + j] = off < S ? (int32_t)((int64_t)(e / L) * S + off) : -1;
+        }
+    }
+    free(cursor);
+
+    if (bad) return ORACLE_BAD_EXPERT;
+    if (over) return ORACLE_CAPACITY;
+    return ORACLE_OK;
+}
+
+/*
+ * Dispatch: copy each token's hidden row to every destination slot it was
+ * given, with its source token index and its top-k weight.
+ *
+ * [SYM] §6.1 passes x, topk_weights and the destination slot array to the
+ * dispatch kernel; [V2] TokenLayout block: a received record holds the hidden
+ * row, the top-k weights and the source token index.  [SYM] §9.2: dispatch
+ * returns recv_x and the received weights.
+ *
+ * Slots < 0 or >= num_rows are skipped.  recv_src_token and recv_weight may
+ * be NULL (not written).  With topk_weights NULL every weight is 1.
+ */
+void oracle_dispatch(int32_t T, int32_t H, int32_t K, int64_t num_rows,
+                     const uint16_t *x, const float *topk_weights,
+                     const int32_t *token_slot, uint16_t *recv_x,
+                     int32_t *recv_src_token, float *recv_weight)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < K; ++j) {
+            int64_t s = token_slot[t * K + j];
+            if (s < 0 || s >= num_rows) continue;
+            memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));
+            if (recv_src_token) recv_src_token[s] = (int32_t)t;
+            if (recv_weight) recv_weight[s] = topk_weights ? topk_weights[t * K + j] : 1.0f;
+        }
+    }
+}
+
+/* bf16 bit pattern -> value (exact). */
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Round a double to the nearest bf16 (8 significant bits, float's exponent
+ * range, gradual underflow), ties to even, overflow to infinity.
+ *
+ * For |v| = m * 2^e with m in [0.5, 1), the bf16 quantum at that magnitude is
+ * 2^(e-8), but never below the subnormal quantum 2^-133.  Scaling by a power
+ * of two is exact, and rint() rounds half to even in the default mode.
+ */
+static uint16_t double_to_bf16(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);
+    int qexp = e - 8;
+    if (qexp < -133) qexp = -133;
+    double r = ldexp(rint(ldexp(a, -qexp)), qexp);
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;
+    float f = (float)r; /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/*
+ * Combine: gather the K expert-output rows of each token from the slots that
+ * dispatch used, weight them by the token's top-k weights and sum.
+ *
+ * [SYM] §9.2: combine takes the expert outputs, the dispatch handle and
+ * topk_weights and returns tokens in their original order.  The sum is taken
+ * in double precision over j = 0..K-1 and rounded once to bf16.  Slots < 0 or
+ * >= num_rows contribute nothing; topk_weights NULL means unit weights.
+ */
+void oracle_combine(int32_t T, int32_t H, int32_t K, int64_t num_rows,
+                    const uint16_t *y, const int32_t *token_slot,
+                    const float *topk_weights, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < K; ++j) {
+                int64_t s = token_slot[t * K + j];
+                if (s < 0 || s >= num_rows) continue;
+                double w = topk_weights ? (double)topk_weights[t * K + j] : 1.0;
+                acc += w * bf16_to_double(y[s * H + h]);
+            }
+            out[t * H + h] = double_to_bf16(acc);
+        }
+    }
+}
+
+/* Element-wise conversions, exported so the tests can pin them. */
+void oracle_double_to_bf16(int64_t n, const double *in, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = double_to_bf16(in[i]);
+}
+
+void oracle_bf16_to_double(int64_t n, const uint16_t *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_double(in[i]);
+}

@@ -1,0 +1,76 @@
+"""The pins reject an oracle with a planted mistake.
+
+Each case copies ep_oracle.c, applies one plausible slip (a wrong index, an
+inclusive instead of exclusive scan, a dropped term, truncation instead of
+round-to-nearest-even, ...), builds it with gcc into a temporary library and
+runs the pin tests against that build.  At least one pin must fail.  This
+runs on the CPU only.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
+
+MUTATIONS = {
+    "rank_of_expert_modulo": ("valid_expert(e, E) && e / L == r", "valid_expert(e, E) && e % R == r"),
+    "inclusive_offset_scan": (
+        "expert_offset[e] = (int32_t)run;\n            run += align_up(expert_count[e], A);",
+        "run += align_up(expert_count[e], A);\n            expert_offset[e] = (int32_t)run;"),
+    "alignment_dropped": ("run += align_up(expert_count[e], A);", "run += expert_count[e];"),
+    "cursor_not_advanced": ("cursor[e] += 1;", ""),
+    "slice_base_from_local": ("(int64_t)(e / L) * S + off", "(int64_t)(e % L) * S + off"),
+    "capacity_off_by_one": ("off < S ?", "off <= S ?"),
+    "weights_reversed": ("(double)topk_weights[t * K + j]", "(double)topk_weights[t * K + (K - 1 - j)]"),
+    "round_by_truncation": ("rint(ldexp(a, -qexp))", "floor(ldexp(a, -qexp))"),
+    "one_bit_too_many": ("int qexp = e - 8;", "int qexp = e - 9;"),
+    "src_index_is_topk_pos": ("recv_src_token[s] = (int32_t)t;", "recv_src_token[s] = (int32_t)j;"),
+    "group_range_shifted": ("for (int32_t r = g * ranks_per_group; r < (g + 1) * ranks_per_group; ++r)",
+                            "for (int32_t r = g; r < g + ranks_per_group; ++r)"),
+    "empty_id_counted_bad": ("if (e == -1) continue;", ""),
+    "row_sum_uses_aligned": ("rows += expert_count[e];", "rows += align_up(expert_count[e], A);"),
+}
+
+
+def _pin_suite():
+    pins.test_golden_handworked_layout()
+    pins.test_golden_handworked_combine()
+    pins.test_golden_rounding_ties()
+    for seed in range(30):
+        pins.test_layout_matches_brute_force(seed)
+    pins.test_negative_bad_id_flags_error()
+    pins.test_workload_layout_invariants("tiny")
+    pins.test_workload_layout_invariants("large16k")
+    pins.test_layout_invariants_with_alignment()
+    pins.test_dispatch_rows_are_copies("tiny")
+    pins.test_unit_weight_combine_is_x_times_k("tiny")
+    pins.test_one_hot_combine_returns_x()
+    pins.test_weighted_combine_matches_numpy_gather("tiny")
+    pins.test_bf16_rounding_matches_torch_on_floats()
+
+
+def test_unmutated_build_passes(tmp_path):
+    lib = tmp_path / "lib_clean.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(lib), SRC, "-lm"])
+    with oracle.use_library(oracle.open_library(str(lib))):
+        _pin_suite()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    before, after = MUTATIONS[name]
+    text = open(SRC).read()
+    assert text.count(before) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(before, after))
+    lib = tmp_path / f"lib_{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(lib), str(src), "-lm"])
+    with oracle.use_library(oracle.open_library(str(lib))):
+        with pytest.raises(AssertionError):
+            np.seterr(all="ignore")
+            _pin_suite()
