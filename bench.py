@@ -1,0 +1,248 @@
+"""Benchmark: MoE layout + dispatch + combine on one MI355X.
+
+One step is one pass of the whole hot path over one batch: ep_get_layout
+(counts, token-to-rank map, offsets, slots), ep_dispatch (row scatter into the
+[R*S, H] receive buffer) and ep_combine (top-k weighted gather-reduce back to
+token order, reading the dispatched buffer as the expert outputs).  Inputs
+are synthetic and seeded (ep_inputs), resident in HBM before timing starts.
+
+Prints ONE JSON line: tokens/s for the whole step, effective HBM bandwidth,
+the roofline of the dominant kernel (timed live with HIP events on the stream
+the kernels run on) and the CPU oracle's throughput on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload prefill4k]
+  python bench.py --copy-probe      # plain device copy: practical HBM ceiling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ep_inputs  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E peak, GB/s (1e9 bytes)
+METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
+KERNEL_SOURCES = ["combine_ep_get_amd/csrc/rows.hip", "combine_ep_get_amd/csrc/layout.hip",
+                  "combine_ep_get_amd/csrc/api.hip", "combine_ep_get_amd/csrc/ep_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(wl, R_is_token_in_rank=True):
+    """Bytes each kernel must move per launch (what the method itself needs).
+
+    layout:   read topk_idx (4TK), write token_slot (4TK) and is_token_in_rank (TR)
+    dispatch: read x (2TH), write K rows per token (2TKH); read slot and weight
+              (8TK), write source index and weight per row (8TK)
+    combine:  read K rows per token (2TKH), write out (2TH); read slot and
+              weight (8TK)
+    """
+    T, H, K, R = wl.T, wl.H, wl.K, wl.R
+    lay = 8 * T * K + (T * R if R_is_token_in_rank else 0)
+    dis = 2 * T * H + 2 * T * K * H + 16 * T * K
+    com = 2 * T * K * H + 2 * T * H + 8 * T * K
+    return {"layout": lay, "dispatch": dis, "combine": com}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    entry = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, S, budget_s=12.0):
+    """Time the CPU oracle (single-threaded C) on whole steps of the workload
+    until about `budget_s` seconds have passed (at least one step)."""
+    import oracle
+
+    rows = wl.R * S
+    recv = np.zeros((rows, wl.H), np.uint16)
+    steps, t_total = 0, 0.0
+    while steps == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, wl.G, wl.A)
+        oracle.dispatch(inp.x, lay.token_slot, rows, inp.topk_weights, recv_x=recv)
+        oracle.combine(recv, lay.token_slot, inp.topk_weights)
+        t_total += time.perf_counter() - t0
+        steps += 1
+    return {
+        "value": wl.T * steps / t_total,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{steps} whole step(s) of the {wl.name} workload (layout+dispatch+combine, "
+                  f"T={wl.T}), single-threaded C oracle, {t_total:.1f} s",
+    }
+
+
+def copy_probe(torch, nbytes=1 << 30, iters=20):
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"probe": "device copy", "bytes": nbytes, "ms": ms, "gbps_read_plus_write": gbps,
+            "frac_of_peak": gbps / PEAK_HBM_GBPS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill4k", choices=sorted(ep_inputs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the hot path; --gpus {args.gpus} is not "
+              "supported (multi-GPU dispatch/combine is not built: one GPU only).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_ep_get_amd as ep
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ep.load()
+
+    if args.copy_probe:
+        print(json.dumps(copy_probe(torch)), flush=True)
+        return
+
+    wl = ep_inputs.WORKLOADS[args.workload]
+    inp = ep_inputs.make_inputs(wl)
+    S = oracle_free_stride = None
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, wl.A, 1)
+    S = ep.ep_rank_stride_hint(p)        # worst-case symmetric slice, as a real buffer is sized
+    p.rank_stride_rows = S
+    del oracle_free_stride
+
+    dev = torch.device("cuda:0")
+    d_idx = torch.from_numpy(inp.topk_idx).to(dev)
+    d_w = torch.from_numpy(inp.topk_weights).to(dev)
+    d_x = torch.from_numpy(inp.x.view(np.int16)).to(dev)
+    bufs = ep.alloc_layout(p, dev)
+    recv = torch.empty((wl.R * S, wl.H), dtype=torch.int16, device=dev)
+    recv_src = torch.empty(wl.R * S, dtype=torch.int32, device=dev)
+    recv_w = torch.empty(wl.R * S, dtype=torch.float32, device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, recv_src, recv_w, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    status = ep.ep_read_status(bufs.workspace, stream)
+    if status != ep.EP_OK:
+        raise RuntimeError(f"layout status {ep.error_string(status)}")
+
+    # timed region: exactly `steps` steps, with per-phase HIP events on the
+    # stream the kernels are launched on
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = events[0][0].elapsed_time(events[-1][3])
+    ms_step = ms_total / args.steps
+    phase_ms = {
+        "layout": float(np.mean([e[0].elapsed_time(e[1]) for e in events])),
+        "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
+        "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
+    }
+    nbytes = algorithmic_bytes(wl)
+    total_bytes = sum(nbytes.values())
+    eff_gbps = total_bytes / (ms_step * 1e-3) / 1e9
+    dominant = max(("dispatch", "combine"), key=lambda k: phase_ms[k])
+    achieved = nbytes[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name, dominant)
+
+    result = {
+        "metric": METRIC,
+        "value": wl.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "R": wl.R,
+                   "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed},
+        "effective_hbm_gbps": eff_gbps,
+        "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
+        "us_per_phase": {k: v * 1e3 for k, v in phase_ms.items()},
+        "us_per_step": ms_step * 1e3,
+        "wall_s_timed": t_wall,
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes": nbytes[dominant],
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, inp, S)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+"""ctypes binding of libepget (include/ep_get.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module turns
+tensors into raw device pointers, fills the ``ep_problem`` struct, passes the
+current HIP stream and raises on error codes.  Loading fails loudly if the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libepget.so")
+
+EP_OK = 0
+EP_ERR_INVALID_ARG = -1
+EP_ERR_HIP = -2
+EP_ERR_CAPACITY = -3
+EP_ERR_BAD_EXPERT = -4
+
+EP_MAX_RANKS = 1024
+EP_MAX_EXPERTS = 2048
+EP_MAX_EXPERTS_PER_RANK = 256
+EP_MAX_TOPK = 32
+
+# Every function the C header declares, checked by the test-suite.
+EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
+           "ep_combine", "ep_read_status", "ep_error_string")
+
+
+class EpError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {error_string(code)} ({code})")
+
+
+class Problem(ctypes.Structure):
+    """``ep_problem``: T, H, E, K, R, G, A and the rank slice stride S."""
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_topk", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("rank_stride_rows", ctypes.c_int64),
+    ]
+
+    @classmethod
+    def make(cls, T, H, E, K, R, G=1, A=1, S=0):
+        return cls(T, H, E, K, R, G, A, 0, S)
+
+    @property
+    def num_rows(self) -> int:
+        return self.num_ranks * self.rank_stride_rows
+
+
+_lib = None
+
+
+def load():
+    """Load libepget.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python -m combine_ep_get_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.ep_workspace_bytes.restype = sz
+        lib.ep_workspace_bytes.argtypes = [P]
+        lib.ep_rank_stride_hint.restype = ctypes.c_int64
+        lib.ep_rank_stride_hint.argtypes = [P]
+        lib.ep_get_layout.restype = ctypes.c_int
+        lib.ep_get_layout.argtypes = [P] + [vp] * 9 + [sz, vp]
+        lib.ep_dispatch.restype = ctypes.c_int
+        lib.ep_dispatch.argtypes = [P] + [vp] * 6 + [vp]
+        lib.ep_combine.restype = ctypes.c_int
+        lib.ep_combine.argtypes = [P] + [vp] * 4 + [vp]
+        lib.ep_read_status.restype = ctypes.c_int
+        lib.ep_read_status.argtypes = [vp, vp]
+        lib.ep_error_string.restype = ctypes.c_char_p
+        lib.ep_error_string.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    """Device pointer of a tensor, a raw integer address, or NULL for None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def error_string(code: int) -> str:
+    return load().ep_error_string(code).decode()
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != EP_OK:
+        raise EpError(rc, where)
+    return rc
+
+
+def ep_workspace_bytes(problem: Problem) -> int:
+    return load().ep_workspace_bytes(ctypes.byref(problem))
+
+
+def ep_rank_stride_hint(problem: Problem) -> int:
+    return load().ep_rank_stride_hint(ctypes.byref(problem))
+
+
+def ep_get_layout(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                  rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                  workspace, workspace_bytes=None, stream=None) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = load().ep_get_layout(ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
+                              _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
+                              _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
+                              _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(rc, "ep_get_layout")
+
+
+def ep_dispatch(problem, x, topk_weights, token_slot, recv_x, recv_src_token=None,
+                recv_weight=None, stream=None) -> int:
+    rc = load().ep_dispatch(ctypes.byref(problem), _ptr(x), _ptr(topk_weights), _ptr(token_slot),
+                            _ptr(recv_x), _ptr(recv_src_token), _ptr(recv_weight), _stream(stream))
+    return _check(rc, "ep_dispatch")
+
+
+def ep_combine(problem, y, token_slot, topk_weights, out, stream=None) -> int:
+    rc = load().ep_combine(ctypes.byref(problem), _ptr(y), _ptr(token_slot), _ptr(topk_weights),
+                           _ptr(out), _stream(stream))
+    return _check(rc, "ep_combine")
+
+
+def ep_read_status(workspace, stream=None) -> int:
+    """Synchronises the stream and returns the layout's device status code."""
+    return load().ep_read_status(_ptr(workspace), _stream(stream))

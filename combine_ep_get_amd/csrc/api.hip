@@ -1,0 +1,178 @@
+// C ABI of libepget (declared in include/ep_get.h): argument validation,
+// workspace sizing and kernel launches.  Nothing here allocates, frees or
+// synchronises, except ep_read_status, which exists to synchronise.
+//
+// Limits are those of "DeepEP V2 ElasticBuffer 架构深度分析" (the
+// kNumMaxRanks / kNumMaxExperts / kNumMaxExpertsPerRank block); argument
+// checks before launch play the role of the host asserts that the pages'
+// runtime uses ("DeepEP Symmetric Memory 全面架构分析" §7.3, §9.1).
+#include <limits.h>
+
+#include "../../include/ep_get.h"
+#include "ep_internal.h"
+
+namespace {
+
+using epget::WsLayout;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Checks every field that does not depend on S.
+int check_shape(const ep_problem *p) {
+    if (!p) return EP_ERR_INVALID_ARG;
+    if (p->reserved != 0) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens < 0) return EP_ERR_INVALID_ARG;
+    if (p->hidden < 8 || p->hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+    if (p->num_experts < 1 || p->num_experts > EP_MAX_EXPERTS) return EP_ERR_INVALID_ARG;
+    if (p->num_ranks < 1 || p->num_ranks > EP_MAX_RANKS) return EP_ERR_INVALID_ARG;
+    if (p->num_experts % p->num_ranks != 0) return EP_ERR_INVALID_ARG;
+    if (p->num_experts / p->num_ranks > EP_MAX_EXPERTS_PER_RANK) return EP_ERR_INVALID_ARG;
+    if (p->num_groups < 1 || p->num_ranks % p->num_groups != 0) return EP_ERR_INVALID_ARG;
+    if (p->num_topk < 1 || p->num_topk > EP_MAX_TOPK) return EP_ERR_INVALID_ARG;
+    if (p->expert_alignment < 1) return EP_ERR_INVALID_ARG;
+    const int64_t entries = static_cast<int64_t>(p->num_tokens) * p->num_topk;
+    const int64_t pad = static_cast<int64_t>(p->num_experts) * p->expert_alignment;
+    if (entries + pad > INT32_MAX) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+int check_problem(const ep_problem *p) {
+    const int rc = check_shape(p);
+    if (rc != EP_OK) return rc;
+    if (p->rank_stride_rows < 1) return EP_ERR_INVALID_ARG;
+    if (p->rank_stride_rows * p->num_ranks > INT32_MAX) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+epget::CopyParams copy_params(const ep_problem *p) {
+    epget::CopyParams c;
+    c.T = p->num_tokens;
+    c.H = p->hidden;
+    c.K = p->num_topk;
+    c.nvec = p->hidden / 8;
+    c.vpt = 1;
+    c.num_rows = p->rank_stride_rows * p->num_ranks;
+    return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_workspace_bytes(const ep_problem *p) {
+    if (check_shape(p) != EP_OK) return 0;
+    const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts,
+                                        p->num_ranks, p->num_groups);
+    return static_cast<size_t>(w.bytes);
+}
+
+int64_t ep_rank_stride_hint(const ep_problem *p) {
+    if (check_shape(p) != EP_OK) return -1;
+    const int64_t L = p->num_experts / p->num_ranks;
+    const int64_t per_token = p->num_topk < L ? p->num_topk : L;
+    const int64_t s = p->num_tokens * per_token + L * (p->expert_alignment - 1);
+    return s > 0 ? s : 1;
+}
+
+int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
+                  int32_t *expert_offset, int32_t *rank_row_count, int32_t *rank_token_count,
+                  int32_t *group_token_count, uint8_t *is_token_in_rank, int32_t *token_slot,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    const bool has_tokens = p->num_tokens > 0;
+    if (!expert_count || !expert_offset || !rank_row_count || !rank_token_count || !workspace)
+        return EP_ERR_INVALID_ARG;
+    if (has_tokens && (!topk_idx || !is_token_in_rank || !token_slot)) return EP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(expert_count, 4) || !aligned(expert_offset, 4) ||
+        !aligned(rank_row_count, 4) || !aligned(rank_token_count, 4) ||
+        !aligned(group_token_count, 4) || !aligned(token_slot, 4) || !aligned(workspace, 256))
+        return EP_ERR_INVALID_ARG;
+    const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts,
+                                        p->num_ranks, p->num_groups);
+    if (workspace_bytes < static_cast<size_t>(w.bytes)) return EP_ERR_INVALID_ARG;
+
+    epget::LayoutParams lp;
+    lp.topk_idx = topk_idx;
+    lp.T = p->num_tokens;
+    lp.K = p->num_topk;
+    lp.E = p->num_experts;
+    lp.R = p->num_ranks;
+    lp.G = p->num_groups;
+    lp.A = p->expert_alignment;
+    lp.L = p->num_experts / p->num_ranks;
+    lp.ranks_per_group = p->num_ranks / p->num_groups;
+    lp.S = static_cast<int32_t>(p->rank_stride_rows);
+    lp.chunk_tokens = w.chunk_tokens;
+    lp.nchunks = static_cast<int32_t>(w.nchunks);
+    lp.ncols = w.ncols;
+    lp.pitch = w.pitch;
+    int nbits = 0;
+    while ((1 << nbits) < p->num_experts) ++nbits;
+    lp.nbits = nbits;
+    lp.expert_count = expert_count;
+    lp.expert_offset = expert_offset;
+    lp.rank_row_count = rank_row_count;
+    lp.rank_token_count = rank_token_count;
+    lp.group_token_count = group_token_count;
+    lp.is_token_in_rank = is_token_in_rank;
+    lp.token_slot = token_slot;
+    char *ws = static_cast<char *>(workspace);
+    lp.status = reinterpret_cast<int32_t *>(ws);
+    lp.totals = reinterpret_cast<int32_t *>(ws + w.totals_off);
+    lp.table = reinterpret_cast<int32_t *>(ws + w.table_off);
+    return hip_rc(epget::launch_layout(lp, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch(const ep_problem *p, const uint16_t *x, const float *topk_weights,
+                const int32_t *token_slot, uint16_t *recv_x, int32_t *recv_src_token,
+                float *recv_weight, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!x || !token_slot || !recv_x) return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(token_slot, 4) ||
+        !aligned(topk_weights, 4) || !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
+        return EP_ERR_INVALID_ARG;
+    return hip_rc(epget::launch_dispatch(copy_params(p), x, topk_weights, token_slot, recv_x,
+                                         recv_src_token, recv_weight,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine(const ep_problem *p, const uint16_t *y, const int32_t *token_slot,
+               const float *topk_weights, uint16_t *out, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!y || !token_slot || !out) return EP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(token_slot, 4) ||
+        !aligned(topk_weights, 4))
+        return EP_ERR_INVALID_ARG;
+    return hip_rc(epget::launch_combine(copy_params(p), y, token_slot, topk_weights, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int ep_read_status(const void *workspace, void *stream) {
+    if (!workspace || !aligned(workspace, 4)) return EP_ERR_INVALID_ARG;
+    int32_t v = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return EP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return EP_ERR_HIP;
+    return v;
+}
+
+const char *ep_error_string(int code) {
+    switch (code) {
+        case EP_OK: return "ok";
+        case EP_ERR_INVALID_ARG: return "invalid argument";
+        case EP_ERR_HIP: return "HIP runtime error";
+        case EP_ERR_CAPACITY: return "rank slice capacity exceeded";
+        case EP_ERR_BAD_EXPERT: return "expert id out of range";
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP translation units of libepget.
+// Not part of the public ABI (that is include/ep_get.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epget {
+
+// Entries (token, top-k pairs) per layout chunk.  One wave walks a chunk in
+// 64-entry steps when it assigns slots, and the count tables hold one row per
+// chunk, so this trades slot-walk latency against scan-table size.
+constexpr int kChunkEntries = 1024;
+
+// Workspace layout, all offsets in bytes from the workspace base:
+//   [0, 256)                  status word (int32) + padding
+//   [256, 256 + pitch*4)      column totals of the chunk table
+//   [table_off, ...)          chunk table: nchunks rows x pitch int32
+// Columns of the chunk table: E experts | R ranks | G groups | 1 bad-id count.
+struct WsLayout {
+    int64_t nchunks;      // >= 1
+    int32_t chunk_tokens; // tokens per chunk
+    int32_t ncols;        // E + R + G + 1
+    int32_t pitch;        // ncols rounded up to a multiple of 64
+    int64_t totals_off;
+    int64_t table_off;
+    int64_t bytes;
+};
+
+WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t R, int32_t G);
+
+struct LayoutParams {
+    const int32_t *topk_idx;
+    int32_t T, K, E, R, G, A, L, ranks_per_group;
+    int32_t S;
+    int32_t chunk_tokens, nchunks, ncols, pitch, nbits;
+    int32_t *expert_count, *expert_offset, *rank_row_count, *rank_token_count;
+    int32_t *group_token_count;  // may be null
+    uint8_t *is_token_in_rank;
+    int32_t *token_slot;
+    int32_t *status, *totals, *table;
+};
+
+struct CopyParams {
+    int32_t T, H, K;
+    int32_t nvec;      // H / 8 : 16-byte vectors per row
+    int32_t vpt;       // vectors per thread (<= kMaxVpt)
+    int64_t num_rows;  // R * S
+};
+
+constexpr int kCopyThreads = 128;
+constexpr int kMaxVpt = 8;
+
+hipError_t launch_layout(const LayoutParams &p, hipStream_t stream);
+hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *w,
+                           const int32_t *slot, uint16_t *recv_x, int32_t *recv_src,
+                           float *recv_w, hipStream_t stream);
+hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
+                          const float *w, uint16_t *out, hipStream_t stream);
+
+// Grid shape for the row kernels: (tokens, column splits) and vectors per
+// thread, chosen so that small batches still spread over all CUs.
+void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt);
+
+}  // namespace epget

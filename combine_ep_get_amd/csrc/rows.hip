@@ -1,0 +1,186 @@
+// Row kernels for gfx950: dispatch scatter and weighted combine.
+//
+// Both are pure HBM streaming.  A workgroup owns one token and a contiguous
+// run of 16-byte column vectors of its row; the token's K destination slots
+// and weights are workgroup-uniform, so they live in scalar registers.
+//
+// dispatch ("DeepEP Symmetric Memory 全面架构分析" §6.1 dispatch arguments;
+// the received record of "DeepEP V2 ElasticBuffer 架构深度分析", TokenLayout
+// block): each thread loads its vectors of x[t] once and stores them to all
+// K destination rows — one read, K writes per vector.
+//
+// combine (same first page, §9.2 combine(x, handle, topk_weights)): each
+// thread gathers the K rows' vectors for one column position (K loads in
+// flight), folds them into eight fp32 accumulators in ascending j with fused
+// multiply-add, and rounds once to bf16 (round-to-nearest-even, the
+// hardware's packed bf16 conversion).
+#include "../../include/ep_get.h"
+#include "ep_internal.h"
+
+namespace epget {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bool slot_ok(int32_t s, int64_t num_rows) {
+    return s >= 0 && s < num_rows;
+}
+
+// VPT: 16-byte vectors per thread.  Loads are unconditional (the column is
+// clamped into the row) so the compiler issues them back to back; only the
+// stores are predicated.
+template <int VPT>
+__global__ __launch_bounds__(kCopyThreads) void dispatch_kernel(
+    CopyParams c, const uint16_t *__restrict__ x, const float *__restrict__ w,
+    const int32_t *__restrict__ slot, uint16_t *__restrict__ recv_x,
+    int32_t *__restrict__ recv_src, float *__restrict__ recv_w) {
+    const int t = blockIdx.x;
+    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * c.H);
+    const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    u32x4 buf[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
+    // source index and weight of each received row (written once per token)
+    if (blockIdx.y == 0 && static_cast<int>(threadIdx.x) < c.K) {
+        const int j = threadIdx.x;
+        const int32_t s = srow[j];
+        if (slot_ok(s, c.num_rows)) {
+            if (recv_src) recv_src[s] = t;
+            if (recv_w) recv_w[s] = w ? w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+        }
+    }
+    for (int j = 0; j < c.K; ++j) {
+        const int32_t s = srow[j];
+        if (!slot_ok(s, c.num_rows)) continue;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(recv_x + static_cast<int64_t>(s) * c.H);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int col = v0 + v * kCopyThreads;
+            if (col < c.nvec) dst[col] = buf[v];
+        }
+    }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = static_cast<__bf16>(lo);
+    const __bf16 b = static_cast<__bf16>(hi);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// KG: top-k entries gathered per pass (all KG loads in flight together).  An
+// entry with an invalid slot loads row 0 instead (always in bounds) and its
+// contribution is discarded by a select, so no load sits behind a branch.
+template <int KG>
+__global__ __launch_bounds__(kCopyThreads) void combine_kernel(
+    CopyParams c, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
+    const float *__restrict__ w, uint16_t *__restrict__ out) {
+    const int t = blockIdx.x;
+    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
+    const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H);
+    const int v0 = blockIdx.y * (kCopyThreads * c.vpt) + threadIdx.x;
+    for (int v = 0; v < c.vpt; ++v) {
+        const int col = v0 + v * kCopyThreads;
+        if (col >= c.nvec) break;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j0 = 0; j0 < c.K; j0 += KG) {
+            u32x4 in[KG];
+            bool ok[KG];
+            float wj[KG];
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+                const int j = min(j0 + jj, c.K - 1);
+                const int32_t s = srow[j];
+                ok[jj] = j0 + jj < c.K && slot_ok(s, c.num_rows);
+                wj[jj] = wrow ? wrow[j] : 1.0f;
+                const int64_t row = ok[jj] ? s : 0;
+                in[jj] = reinterpret_cast<const u32x4 *>(y + row * c.H)[col];
+            }
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = __builtin_fmaf(wj[jj], bf16_lo(in[jj][q]), acc[2 * q]);
+                    const float hi = __builtin_fmaf(wj[jj], bf16_hi(in[jj][q]), acc[2 * q + 1]);
+                    acc[2 * q] = ok[jj] ? lo : acc[2 * q];
+                    acc[2 * q + 1] = ok[jj] ? hi : acc[2 * q + 1];
+                }
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        dst[col] = o;
+    }
+}
+
+}  // namespace
+
+void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt) {
+    // Aim for at least ~2048 workgroups (8 per CU) so that decode-sized
+    // batches still cover the chip; large batches get one workgroup per token
+    // and several vectors per thread.
+    const int64_t want_blocks = 2048;
+    int64_t need = T >= want_blocks ? 1 : (want_blocks + (T > 0 ? T : 1) - 1) / (T > 0 ? T : 1);
+    int64_t v = (nvec + kCopyThreads * need - 1) / (kCopyThreads * need);
+    if (v < 1) v = 1;
+    if (v > kMaxVpt) v = kMaxVpt;
+    *vpt = static_cast<int32_t>(v);
+    *splits = static_cast<int32_t>((nvec + kCopyThreads * v - 1) / (kCopyThreads * v));
+}
+
+hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *w,
+                           const int32_t *slot, uint16_t *recv_x, int32_t *recv_src,
+                           float *recv_w, hipStream_t stream) {
+    int32_t splits, vpt;
+    copy_grid(c.T, c.nvec, &splits, &vpt);
+    CopyParams p = c;
+    p.vpt = vpt;
+    dim3 grid(c.T, splits);
+    switch (vpt) {
+#define EP_DISPATCH_CASE(V)                                                                   \
+    case V:                                                                                   \
+        dispatch_kernel<V><<<grid, kCopyThreads, 0, stream>>>(p, x, w, slot, recv_x, recv_src, \
+                                                              recv_w);                        \
+        break;
+        EP_DISPATCH_CASE(1)
+        EP_DISPATCH_CASE(2)
+        EP_DISPATCH_CASE(3)
+        EP_DISPATCH_CASE(4)
+        EP_DISPATCH_CASE(5)
+        EP_DISPATCH_CASE(6)
+        EP_DISPATCH_CASE(7)
+        EP_DISPATCH_CASE(8)
+#undef EP_DISPATCH_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
+                          const float *w, uint16_t *out, hipStream_t stream) {
+    int32_t splits, vpt;
+    copy_grid(c.T, c.nvec, &splits, &vpt);
+    CopyParams p = c;
+    p.vpt = vpt;
+    dim3 grid(c.T, splits);
+    if (c.K <= 1) {
+        combine_kernel<1><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+    } else if (c.K <= 2) {
+        combine_kernel<2><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+    } else if (c.K <= 4) {
+        combine_kernel<4><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+    } else {
+        combine_kernel<8><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace epget

@@ -136,6 +136,13 @@ def expert_outputs(rows: int, H: int, seed: int) -> np.ndarray:
     return bf16_normal(rng, (rows, H))
 
 
+def permuted_rows(rows: np.ndarray, seed: int) -> np.ndarray:
+    """A seeded row permutation of ``rows`` (stand-in expert outputs that mix
+    different tokens' activations without drawing new normals)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x9E]))
+    return rows[rng.permutation(rows.shape[0])]
+
+
 def random_small_case(rng: np.random.Generator, *, max_T=64, max_E=16, max_K=6,
                       allow_empty=True, allow_duplicates=False):
     """A random tiny routing problem for brute-force checks.

@@ -1,0 +1,183 @@
+/*
+ * ep_get.h — C ABI of libepget: MoE token layout, dispatch and combine for
+ * one source rank on one MI355X (gfx950), with the R destination ranks held
+ * as fixed-stride slices of one receive buffer.
+ *
+ * Pages cited (by title):
+ *   [SYM] "DeepEP Symmetric Memory 全面架构分析"
+ *         (DeepEP symmetric memory: full architecture analysis)
+ *   [V2]  "DeepEP V2 ElasticBuffer 架构深度分析"
+ *         (DeepEP V2 ElasticBuffer architecture in depth; no section headings,
+ *         its code blocks are cited by what they show)
+ *   [V1]  "第 3 章 V1：Buffer 初始化与通信域建立"
+ *         (chapter 3, V1 buffer initialisation and communicator set-up)
+ *
+ * Conventions for every entry point:
+ *   - All pointers named "device" point to device memory the caller owns
+ *     (allocated e.g. by PyTorch); the library allocates and frees nothing
+ *     and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  The hot
+ *     calls (ep_get_layout, ep_dispatch, ep_combine) only enqueue kernels:
+ *     they never synchronise, so their results are ready when the stream
+ *     reaches that point.
+ *   - Return value: EP_OK, or a negative EP_ERR_* code.  Argument problems
+ *     are found on the host before anything is enqueued (EP_ERR_INVALID_ARG);
+ *     a failed launch gives EP_ERR_HIP.  Problems only the device can see (an
+ *     expert id out of range, a slice overflow) are written to a status word
+ *     in the workspace that ep_read_status returns.  This is the C form of
+ *     the host asserts and the exception with line info that [SYM] §7.3 and
+ *     [V2] (pp_send/pp_recv block) show.
+ *
+ * Notation, following the dispatch launch arguments of [SYM] §6.1:
+ *   T num_tokens, H hidden, E num_experts, K num_topk, R num_ranks
+ *   (scale-up ranks), G num_groups, A expert_alignment, S rank_stride_rows,
+ *   L = E / R local experts per rank, rank(e) = e / L,
+ *   group(r) = r / (R / G).
+ *
+ * Receive buffer: slice r occupies rows [r*S, (r+1)*S) of an [R*S, H] bf16
+ * array — the same byte offset in every rank's symmetric buffer, as [SYM]
+ * §5.1 maps one symmetric offset to each peer.  Inside slice r the experts of
+ * rank r own consecutive segments in local-expert order; expert e's segment
+ * starts at row expert_offset[e] (aligned to A) and holds its rows in
+ * ascending source token, then ascending top-k position.
+ */
+#ifndef EP_GET_H
+#define EP_GET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_OK 0
+#define EP_ERR_INVALID_ARG (-1) /* bad sizes, limits, NULL or misaligned pointer, small workspace */
+#define EP_ERR_HIP (-2)         /* a HIP runtime call or kernel launch failed */
+#define EP_ERR_CAPACITY (-3)    /* some rank needs more than S rows (device-detected) */
+#define EP_ERR_BAD_EXPERT (-4)  /* an id outside [0,E) other than -1 (device-detected) */
+
+/* Limits of [V2] (kNumMaxRanks, kNumMaxExperts, kNumMaxExpertsPerRank)
+ * and this library's own top-k limit. */
+#define EP_MAX_RANKS 1024
+#define EP_MAX_EXPERTS 2048
+#define EP_MAX_EXPERTS_PER_RANK 256
+#define EP_MAX_TOPK 32
+
+/* Problem description shared by all calls.  Valid when:
+ *   T >= 0; H >= 8 and H % 8 == 0 (rows are whole 16-byte vectors);
+ *   1 <= E <= 2048; 1 <= R <= 1024; E % R == 0; E / R <= 256;
+ *   1 <= G and R % G == 0; 1 <= K <= 32; A >= 1;
+ *   S >= 1; R * S <= INT32_MAX (slots are int32);
+ *   T * K + E * A <= INT32_MAX. */
+typedef struct ep_problem {
+    int32_t num_tokens;       /* T: tokens of this source rank */
+    int32_t hidden;           /* H: bf16 elements per row */
+    int32_t num_experts;      /* E */
+    int32_t num_topk;         /* K */
+    int32_t num_ranks;        /* R: destination ranks (slices) */
+    int32_t num_groups;       /* G: scale-out groups, 1 unless hierarchical */
+    int32_t expert_alignment; /* A: segment starts are multiples of A ([SYM] §6.1) */
+    int32_t reserved;         /* must be 0 */
+    int64_t rank_stride_rows; /* S: rows per rank slice, the same for every rank */
+} ep_problem;
+
+/* Bytes of device workspace ep_get_layout needs for this problem (chunk
+ * count tables and the status word), or 0 if the problem is invalid.  The
+ * workspace must be 256-byte aligned; its contents need no initialisation. */
+size_t ep_workspace_bytes(const ep_problem *problem);
+
+/* Worst-case rows one source rank can put in one slice, ignoring
+ * problem->rank_stride_rows: T * min(K, L) + L * (A - 1).  The analogue of
+ * sizing the buffer from num_max_tokens_per_rank ([SYM] §9.1, §9.5
+ * get_buffer_size_hint).  Returns -1 if the problem is otherwise invalid. */
+int64_t ep_rank_stride_hint(const ep_problem *problem);
+
+/* Routing layout: the counts, prefix sums and per-entry destination slots
+ * that [SYM] §6.1 passes to the dispatch kernel (per-scale-up-rank and
+ * per-expert prefix sums, unaligned per-expert counts, dst_buffer_slot_idx)
+ * and that [SYM] §7.3 reads back per rank and per local expert.
+ *
+ * Input:
+ *   topk_idx [T,K] int32 device, row-major; -1 marks an empty entry.
+ * Outputs (device, caller-allocated, fully overwritten):
+ *   expert_count      [E] int32  rows routed to each expert (the unaligned
+ *                                per-expert receive count)
+ *   expert_offset     [E] int32  first row of expert e's segment inside slice
+ *                                rank(e): sum over lower local experts of the
+ *                                same rank of align_up(expert_count, A)
+ *   rank_row_count    [R] int32  expanded rows per rank (sum of its experts'
+ *                                counts; all of them sum to the number of
+ *                                valid entries)
+ *   rank_token_count  [R] int32  tokens with at least one entry on the rank
+ *   group_token_count [G] int32  tokens with at least one entry in the group
+ *                                ([V1] §3.2 groups ranks by eight); may be NULL
+ *   is_token_in_rank  [T,R] uint8 1 if token t has an entry on rank r, else 0
+ *   token_slot        [T,K] int32 destination row of entry (t,j) in the
+ *                                [R*S,H] receive buffer: rank(e)*S +
+ *                                expert_offset[e] + (number of earlier entries,
+ *                                token-major, naming the same expert); -1 for
+ *                                empty or invalid ids and for rows at or past
+ *                                S inside their slice.  This is the handle
+ *                                ep_dispatch and ep_combine take ([SYM] §9.2).
+ *   workspace         ep_workspace_bytes(problem) bytes, device.
+ * Device-detected errors (read with ep_read_status): an id outside [0,E)
+ * other than -1 gives EP_ERR_BAD_EXPERT and is treated as empty; a rank whose
+ * aligned rows exceed S gives EP_ERR_CAPACITY and its excess rows get slot -1.
+ * The bad-id error is reported in preference to the capacity error.  Each
+ * call overwrites the status. */
+int ep_get_layout(const ep_problem *problem, const int32_t *topk_idx,
+                  int32_t *expert_count, int32_t *expert_offset,
+                  int32_t *rank_row_count, int32_t *rank_token_count,
+                  int32_t *group_token_count, uint8_t *is_token_in_rank,
+                  int32_t *token_slot, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* Dispatch: recv_x[token_slot[t,j], :] = x[t, :] (bit copy), plus
+ * recv_src_token[slot] = t and recv_weight[slot] = topk_weights[t,j] — the
+ * hidden row, source token index and top-k weight that the received token
+ * record of [V2] (TokenLayout block) carries; [SYM] §6.1 lists x,
+ * topk_weights and dst_buffer_slot_idx among the dispatch arguments.
+ *
+ *   x              [T,H] bf16 (raw uint16) device, 16-byte aligned
+ *   topk_weights   [T,K] fp32 device, or NULL (every weight is 1)
+ *   token_slot     [T,K] int32 device, from ep_get_layout
+ *   recv_x         [R*S,H] bf16 device, 16-byte aligned
+ *   recv_src_token [R*S] int32 device, or NULL (not written)
+ *   recv_weight    [R*S] fp32 device, or NULL (not written)
+ * Slots outside [0, R*S) are skipped.  Rows that no slot names (alignment
+ * padding, unused capacity) are left untouched. */
+int ep_dispatch(const ep_problem *problem, const uint16_t *x,
+                const float *topk_weights, const int32_t *token_slot,
+                uint16_t *recv_x, int32_t *recv_src_token, float *recv_weight,
+                void *stream);
+
+/* Combine: out[t,h] = bf16(sum_{j<K} w[t,j] * y[token_slot[t,j], h]), with an
+ * fp32 accumulator folded in ascending j by fused multiply-add and one
+ * round-to-nearest-even to bf16 — the top-k-weighted reduction that [SYM]
+ * §9.2's combine(x, handle, topk_weights) performs back into token order.
+ *
+ *   y            [R*S,H] bf16 device (expert outputs in the receive layout),
+ *                16-byte aligned
+ *   token_slot   [T,K] int32 device, from ep_get_layout
+ *   topk_weights [T,K] fp32 device, or NULL (unit weights)
+ *   out          [T,H] bf16 device, 16-byte aligned
+ * Slots outside [0, R*S) contribute nothing; a token with no valid slot
+ * gets zeros. */
+int ep_combine(const ep_problem *problem, const uint16_t *y,
+               const int32_t *token_slot, const float *topk_weights,
+               uint16_t *out, void *stream);
+
+/* Synchronises `stream`, then returns the status word the last
+ * ep_get_layout on that workspace wrote (EP_OK, EP_ERR_BAD_EXPERT or
+ * EP_ERR_CAPACITY), or EP_ERR_HIP / EP_ERR_INVALID_ARG if it cannot read it. */
+int ep_read_status(const void *workspace, void *stream);
+
+/* Static, human-readable name of an EP_* code. */
+const char *ep_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_GET_H */

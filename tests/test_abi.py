@@ -1,0 +1,87 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function the header declares, and rejects invalid problems before it
+enqueues anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_ep_get_amd as ep
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ep_get.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == set(ep.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ep.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    assert ep.error_string(ep.EP_OK) == "ok"
+    assert "capacity" in ep.error_string(ep.EP_ERR_CAPACITY)
+    assert "expert" in ep.error_string(ep.EP_ERR_BAD_EXPERT)
+
+
+def P(**kw):
+    base = dict(T=4096, H=7168, E=256, K=8, R=8, G=1, A=1, S=32768)
+    base.update(kw)
+    return ep.Problem.make(**base)
+
+
+def test_stride_hint_and_workspace():
+    assert ep.ep_rank_stride_hint(P()) == 4096 * 8
+    assert ep.ep_rank_stride_hint(P(E=16, R=4, K=4, T=128)) == 128 * 4
+    assert ep.ep_rank_stride_hint(P(E=64, R=16, K=8, T=100)) == 100 * 4   # min(K, L) = 4
+    assert ep.ep_rank_stride_hint(P(A=8)) == 4096 * 8 + 32 * 7
+    assert ep.ep_workspace_bytes(P()) > 0
+    assert ep.ep_workspace_bytes(P(T=0)) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(E=255), dict(E=4096, R=8), dict(R=2048, E=2048), dict(E=1024, R=2),   # limits
+    dict(K=0), dict(K=33), dict(H=7), dict(H=0), dict(T=-1), dict(G=3), dict(G=0),
+    dict(A=0), dict(S=0), dict(S=2**31 // 8 + 1),
+])
+def test_invalid_problems_rejected_before_launch(bad):
+    p = P(**bad)
+    lib = ep.load()
+    fake = 1 << 20   # never dereferenced: validation fails first
+    rc = lib.ep_get_layout(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                           fake, 1 << 30, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_combine(ctypes.byref(p), fake, fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_reserved_field_must_be_zero():
+    p = P()
+    p.reserved = 1
+    assert ep.ep_workspace_bytes(p) == 0
+
+
+def test_bad_pointers_rejected():
+    p = P()
+    lib = ep.load()
+    a = 1 << 20
+    # misaligned x
+    assert lib.ep_dispatch(ctypes.byref(p), a + 2, a, a, a, a, a, None) == ep.EP_ERR_INVALID_ARG
+    # NULL output
+    assert lib.ep_combine(ctypes.byref(p), a, a, a, None, None) == ep.EP_ERR_INVALID_ARG
+    # workspace too small or misaligned
+    need = ep.ep_workspace_bytes(p)
+    args = [a] * 8
+    assert lib.ep_get_layout(ctypes.byref(p), *args, a, need - 1, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(ctypes.byref(p), *args, a + 16, need, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_read_status(None, None) == ep.EP_ERR_INVALID_ARG

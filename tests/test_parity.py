@@ -1,0 +1,277 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Layout outputs, slots and dispatched rows must match bit for bit; the bf16
+combine output must satisfy |gpu - oracle| <= 1e-3 + 1e-2*|oracle| on every
+element (the oracle sums in fp64, the kernel in fp32 with FMA).
+"""
+import numpy as np
+import pytest
+import torch
+
+import ep_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def ep():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import combine_ep_get_amd as ep
+    ep.load()
+    return ep
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_dev(a_u16):
+    return dev(a_u16.view(np.int16))
+
+
+def host_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def gpu_layout(ep, idx, E, R, S, G=1, A=1, H=8):
+    T, K = idx.shape
+    p = ep.Problem.make(T, H, E, K, R, G, A, S)
+    bufs = ep.alloc_layout(p)
+    d_idx = dev(idx) if T else torch.empty((0, K), dtype=torch.int32, device="cuda")
+    ep.ep_get_layout(p, d_idx, *bufs.args())
+    status = ep.ep_read_status(bufs.workspace)
+    return p, bufs, status
+
+
+def assert_layout_matches(ep, bufs, status, ref):
+    code = {oracle.OK: ep.EP_OK, oracle.CAPACITY: ep.EP_ERR_CAPACITY,
+            oracle.BAD_EXPERT: ep.EP_ERR_BAD_EXPERT}[ref.status]
+    assert status == code
+    for name in ("expert_count", "expert_offset", "rank_row_count", "rank_token_count",
+                 "group_token_count", "is_token_in_rank", "token_slot"):
+        np.testing.assert_array_equal(getattr(bufs, name).cpu().numpy(), getattr(ref, name),
+                                      err_msg=name)
+
+
+def combine_close(got_u16, ref_u16):
+    g = oracle.bf16_to_double(got_u16)
+    r = oracle.bf16_to_double(ref_u16)
+    bad = ~(np.abs(g - r) <= ATOL + RTOL * np.abs(r))
+    assert not bad.any(), f"{bad.sum()} combine elements out of tolerance, first at {np.argwhere(bad)[:3]}"
+
+
+def tight_stride(ref_counts, E, R, A=1):
+    L = E // R
+    aligned = -(-ref_counts // A) * A
+    return int(max(1, aligned.reshape(R, L).sum(1).max()))
+
+
+def run_full(ep, idx, w, x, E, R, G, A, S, y=None, check_src=True):
+    """Layout + dispatch + combine on both sides; returns nothing, asserts."""
+    T, K = idx.shape
+    H = x.shape[1]
+    ref = oracle.layout(idx, E, R, S, G, A)
+    p, bufs, status = gpu_layout(ep, idx, E, R, S, G, A, H)
+    assert_layout_matches(ep, bufs, status, ref)
+    rows = R * S
+    # dispatch
+    d_x, d_w = bf16_dev(x), dev(w)
+    recv = torch.empty((rows, H), dtype=torch.int16, device="cuda")
+    src = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    rw = torch.full((rows,), -7.0, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, src, rw)
+    torch.cuda.synchronize()
+    ref_rx, ref_src, ref_rw = oracle.dispatch(x, ref.token_slot, rows, w)
+    s = ref.token_slot.ravel()
+    s = s[s >= 0]
+    got_rx = host_u16(recv)
+    np.testing.assert_array_equal(got_rx[s], ref_rx[s])
+    if check_src:
+        np.testing.assert_array_equal(src.cpu().numpy()[s], ref_src[s])
+        np.testing.assert_array_equal(rw.cpu().numpy()[s], ref_rw[s])
+    # combine on expert outputs in the receive layout
+    if y is None:
+        y = ep_inputs.permuted_rows(ref_rx, seed=11)
+    d_y = bf16_dev(y)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(p, d_y, bufs.token_slot, d_w, out)
+    out_unit = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(p, d_y, bufs.token_slot, None, out_unit)
+    torch.cuda.synchronize()
+    combine_close(host_u16(out), oracle.combine(y, ref.token_slot, w))
+    combine_close(host_u16(out_unit), oracle.combine(y, ref.token_slot, None))
+    return ref, bufs, got_rx
+
+
+# --------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["tiny", "decode128", "prefill4k", "zipf8k", "large16k"])
+def test_workload_parity(ep, name):
+    print(f"[parity] workload={name}", flush=True)
+    inp = ep_inputs.make_inputs(name)
+    wl = inp.wl
+    counts = np.bincount(inp.topk_idx.ravel(), minlength=wl.E)
+    S = tight_stride(counts, wl.E, wl.R)
+    y = None
+    if name in ("tiny", "decode128"):
+        y = ep_inputs.expert_outputs(wl.R * S, wl.H, seed=3)
+    run_full(ep, inp.topk_idx, inp.topk_weights, inp.x, wl.E, wl.R, wl.G, wl.A, S, y=y)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode128", "prefill4k", "zipf8k", "large16k"])
+def test_workload_layout_at_default_stride(ep, name):
+    """Layout at the worst-case slice stride the benchmark uses."""
+    inp = ep_inputs.make_inputs(name, with_x=False)
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    ref = oracle.layout(inp.topk_idx, wl.E, wl.R, S, wl.G)
+    p, bufs, status = gpu_layout(ep, inp.topk_idx, wl.E, wl.R, S, wl.G)
+    assert ep.ep_rank_stride_hint(p) == S
+    assert_layout_matches(ep, bufs, status, ref)
+
+
+def test_unit_weight_combine_of_dispatch_is_x_times_k(ep):
+    inp = ep_inputs.make_inputs("prefill4k")
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, 1, S)
+    bufs = ep.alloc_layout(p)
+    ep.ep_get_layout(p, dev(inp.topk_idx), *bufs.args())
+    recv = torch.empty((wl.R * S, wl.H), dtype=torch.int16, device="cuda")
+    d_x = bf16_dev(inp.x)
+    ep.ep_dispatch(p, d_x, None, bufs.token_slot, recv)
+    out = torch.empty_like(d_x)
+    ep.ep_combine(p, recv, bufs.token_slot, None, out)
+    torch.cuda.synchronize()
+    xk = (d_x.view(torch.bfloat16).float() * wl.K).to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(out, xk)
+
+
+# --------------------------------------------------------------- edge cases
+
+def _route_uniform(rng, T, E, K):
+    return np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32) if T else \
+        np.zeros((0, K), np.int32)
+
+
+def _case(ep, idx, E, R, G=1, A=1, S=None, H=64, seed=0):
+    rng = np.random.default_rng(seed)
+    T, K = idx.shape
+    if S is None:
+        counts = np.bincount(idx[(idx >= 0) & (idx < E)].ravel(), minlength=E)
+        S = tight_stride(counts, E, R, A) + 5
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    return run_full(ep, idx, w, x, E, R, G, A, S)
+
+
+def test_single_token(ep):
+    _case(ep, np.array([[5, 1, 9, 14]], np.int32), E=16, R=4, H=256)
+
+
+def test_topk_equals_local_experts(ep):
+    rng = np.random.default_rng(1)
+    E, R = 32, 8
+    idx = _route_uniform(rng, 300, E, E // R)
+    _case(ep, idx, E, R, H=128)
+
+
+def test_all_tokens_to_the_same_experts(ep):
+    T, K = 3000, 8  # several chunks, every entry on experts 0..7 (rank 0)
+    idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    ref, bufs, _ = _case(ep, idx, E=64, R=8, H=64)
+    assert (bufs.rank_row_count.cpu().numpy()[1:] == 0).all()
+
+
+def test_one_rank_empty(ep):
+    rng = np.random.default_rng(2)
+    E, R, T, K = 64, 8, 2500, 6
+    idx = np.stack([rng.choice(np.arange(8, 64), K, replace=False) for _ in range(T)]).astype(np.int32)
+    ref, bufs, _ = _case(ep, idx, E, R, H=64)
+    assert bufs.rank_token_count.cpu().numpy()[0] == 0
+
+
+@pytest.mark.parametrize("A", [2, 4, 128])
+def test_expert_alignment(ep, A):
+    rng = np.random.default_rng(A)
+    idx = _route_uniform(rng, 1500, 64, 8)
+    _case(ep, idx, 64, 8, A=A, H=64)
+
+
+def test_empty_entries_and_duplicates(ep):
+    rng = np.random.default_rng(4)
+    idx = rng.integers(0, 48, size=(2100, 5)).astype(np.int32)   # duplicates allowed
+    idx[rng.random(idx.shape) < 0.2] = -1
+    _case(ep, idx, 48, 6, G=3, H=72)
+
+
+def test_capacity_exact_and_one_short(ep):
+    rng = np.random.default_rng(5)
+    E, R, A = 64, 8, 4
+    idx = _route_uniform(rng, 1200, E, 8)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    S = tight_stride(counts, E, R, A)
+    ref, _, _ = _case(ep, idx, E, R, A=A, S=S, H=64)
+    assert ref.status == oracle.OK
+    ref, _, _ = _case(ep, idx, E, R, A=A, S=S - 1, H=64)
+    assert ref.status == oracle.CAPACITY
+
+
+def test_bad_expert_id(ep):
+    rng = np.random.default_rng(6)
+    idx = _route_uniform(rng, 1100, 32, 4)
+    idx[17, 2] = 32
+    idx[900, 0] = -5
+    ref, _, _ = _case(ep, idx, 32, 4, H=64)
+    assert ref.status == oracle.BAD_EXPERT
+
+
+def test_empty_batch(ep):
+    idx = np.zeros((0, 4), np.int32)
+    p, bufs, status = gpu_layout(ep, idx, 16, 4, 8, H=64)
+    assert status == ep.EP_OK
+    ref = oracle.layout(idx, 16, 4, 8)
+    assert_layout_matches(ep, bufs, status, ref)
+    # dispatch/combine of nothing is a no-op
+    ep.ep_dispatch(p, None, None, None, None)
+    ep.ep_combine(p, None, None, None, None)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(ep, seed):
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.choice([1, 2, 4, 8, 16]))
+    L = int(rng.choice([1, 3, 8, 32]))
+    E = R * L
+    K = int(rng.integers(1, min(E, 12) + 1))
+    T = int(rng.choice([1, 7, 129, 1000, 3333, 7001]))
+    G = int(rng.choice([g for g in (1, 2, 4) if R % g == 0]))
+    A = int(rng.choice([1, 1, 2, 8]))
+    H = 8 * int(rng.integers(1, 200))
+    idx = _route_uniform(rng, T, E, K)
+    print(f"[parity] random seed={seed} T={T} H={H} E={E} K={K} R={R} G={G} A={A}", flush=True)
+    _case(ep, idx, E, R, G=G, A=A, H=H, seed=seed)
+
+
+def test_large_expert_count_and_rank_count(ep):
+    rng = np.random.default_rng(8)
+    E, R, K, T = 2048, 1024, 32, 1500
+    idx = _route_uniform(rng, T, E, K)
+    _case(ep, idx, E, R, H=16)
+    E, R = 2048, 8   # 256 local experts per rank
+    _case(ep, _route_uniform(rng, T, E, K), E, R, H=16)
+
+
+def test_repeatable(ep):
+    inp = ep_inputs.make_inputs("zipf8k", with_x=False)
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    outs = []
+    for _ in range(3):
+        _, bufs, _ = gpu_layout(ep, inp.topk_idx, wl.E, wl.R, S)
+        outs.append(bufs.token_slot.cpu().numpy())
+    assert all((o == outs[0]).all() for o in outs)
