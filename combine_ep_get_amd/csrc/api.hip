@@ -104,6 +104,9 @@ int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
     lp.A = p->expert_alignment;
     lp.L = p->num_experts / p->num_ranks;
     lp.ranks_per_group = p->num_ranks / p->num_groups;
+    lp.div_L = epget::FastDiv::make(static_cast<uint32_t>(lp.L));
+    lp.div_R = epget::FastDiv::make(static_cast<uint32_t>(lp.R));
+    lp.div_G = epget::FastDiv::make(static_cast<uint32_t>(lp.G));
     lp.S = static_cast<int32_t>(p->rank_stride_rows);
     lp.chunk_tokens = w.chunk_tokens;
     lp.nchunks = static_cast<int32_t>(w.nchunks);

@@ -29,9 +29,22 @@ struct WsLayout {
 
 WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t R, int32_t G);
 
+// Division by a runtime divisor d <= 1024 of dividends n < 2^22 as a
+// multiply-high with m = ceil(2^32 / d); exact on that whole range (checked
+// exhaustively), and a handful of instructions instead of the generic
+// reciprocal-and-correct sequence.
+struct FastDiv {
+    uint64_t m;
+    static FastDiv make(uint32_t d) { return FastDiv{((1ull << 32) + d - 1) / d}; }
+    __device__ __forceinline__ uint32_t operator()(uint32_t n) const {
+        return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 32);
+    }
+};
+
 struct LayoutParams {
     const int32_t *topk_idx;
     int32_t T, K, E, R, G, A, L, ranks_per_group;
+    FastDiv div_L, div_R, div_G;
     int32_t S;
     int32_t chunk_tokens, nchunks, ncols, pitch, nbits;
     int32_t *expert_count, *expert_offset, *rank_row_count, *rank_token_count;
@@ -48,8 +61,9 @@ struct CopyParams {
     int64_t num_rows;  // R * S
 };
 
-constexpr int kCopyThreads = 128;
-constexpr int kMaxVpt = 8;
+constexpr int kCopyThreads = 128;      // dispatch workgroup size
+constexpr int kMaxVpt = 8;            // dispatch vectors per thread
+constexpr int kCombineMaxThreads = 1024;
 
 hipError_t launch_layout(const LayoutParams &p, hipStream_t stream);
 hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *w,
@@ -61,5 +75,8 @@ hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t 
 // Grid shape for the row kernels: (tokens, column splits) and vectors per
 // thread, chosen so that small batches still spread over all CUs.
 void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt);
+// Grid of the combine: (tokens, row pieces) and threads per workgroup (one
+// 16-byte column vector per thread).
+void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads);
 
 }  // namespace epget

@@ -72,52 +72,56 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// KG: top-k entries gathered per pass (all KG loads in flight together).  An
-// entry with an invalid slot loads row 0 instead (always in bounds) and its
-// contribution is discarded by a select, so no load sits behind a branch.
+// One thread per 16-byte column vector: a workgroup covers a whole row (or a
+// contiguous piece of it for small batches), so each thread makes exactly
+// one pass.  KG: top-k entries gathered per round (all KG loads in flight).
+// An entry with an invalid slot loads row 0 instead (always in bounds) and
+// its contribution is discarded by a select, so no load sits behind a
+// branch.  The gathered rows and the output row are touched once, so loads
+// and stores carry the non-temporal hint (measured: it keeps the dispatch's
+// freshly written rows from being evicted and written back while combine
+// streams through them).
 template <int KG>
-__global__ __launch_bounds__(kCopyThreads) void combine_kernel(
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     CopyParams c, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
     const float *__restrict__ w, uint16_t *__restrict__ out) {
     const int t = blockIdx.x;
     const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
     const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
-    u32x4 *dst = reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H);
-    const int v0 = blockIdx.y * (kCopyThreads * c.vpt) + threadIdx.x;
-    for (int v = 0; v < c.vpt; ++v) {
-        const int col = v0 + v * kCopyThreads;
-        if (col >= c.nvec) break;
-        float acc[8];
+    const int col = blockIdx.y * blockDim.x + threadIdx.x;
+    const int colc = min(col, c.nvec - 1);
+    float acc[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j0 = 0; j0 < c.K; j0 += KG) {
-            u32x4 in[KG];
-            bool ok[KG];
-            float wj[KG];
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j0 = 0; j0 < c.K; j0 += KG) {
+        u32x4 in[KG];
+        bool ok[KG];
+        float wj[KG];
 #pragma unroll
-            for (int jj = 0; jj < KG; ++jj) {
-                const int j = min(j0 + jj, c.K - 1);
-                const int32_t s = srow[j];
-                ok[jj] = j0 + jj < c.K && slot_ok(s, c.num_rows);
-                wj[jj] = wrow ? wrow[j] : 1.0f;
-                const int64_t row = ok[jj] ? s : 0;
-                in[jj] = reinterpret_cast<const u32x4 *>(y + row * c.H)[col];
-            }
+        for (int jj = 0; jj < KG; ++jj) {
+            const int j = min(j0 + jj, c.K - 1);
+            const int32_t s = srow[j];
+            ok[jj] = j0 + jj < c.K && slot_ok(s, c.num_rows);
+            wj[jj] = wrow ? wrow[j] : 1.0f;
+            const int64_t row = ok[jj] ? s : 0;
+            in[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + row * c.H) + colc);
+        }
 #pragma unroll
-            for (int jj = 0; jj < KG; ++jj) {
+        for (int jj = 0; jj < KG; ++jj) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float lo = __builtin_fmaf(wj[jj], bf16_lo(in[jj][q]), acc[2 * q]);
-                    const float hi = __builtin_fmaf(wj[jj], bf16_hi(in[jj][q]), acc[2 * q + 1]);
-                    acc[2 * q] = ok[jj] ? lo : acc[2 * q];
-                    acc[2 * q + 1] = ok[jj] ? hi : acc[2 * q + 1];
-                }
+            for (int q = 0; q < 4; ++q) {
+                const float lo = __builtin_fmaf(wj[jj], bf16_lo(in[jj][q]), acc[2 * q]);
+                const float hi = __builtin_fmaf(wj[jj], bf16_hi(in[jj][q]), acc[2 * q + 1]);
+                acc[2 * q] = ok[jj] ? lo : acc[2 * q];
+                acc[2 * q + 1] = ok[jj] ? hi : acc[2 * q + 1];
             }
         }
+    }
+    if (col < c.nvec) {
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-        dst[col] = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H) + col);
     }
 }
 
@@ -134,6 +138,21 @@ void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt) {
     if (v > kMaxVpt) v = kMaxVpt;
     *vpt = static_cast<int32_t>(v);
     *splits = static_cast<int32_t>((nvec + kCopyThreads * v - 1) / (kCopyThreads * v));
+}
+
+void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
+    // One thread per column vector.  A workgroup takes a whole row when the
+    // batch alone gives enough workgroups; otherwise rows are cut into
+    // pieces of at least one wave so that about 2048 workgroups run.
+    const int64_t want_blocks = 2048;
+    const int64_t t = T > 0 ? T : 1;
+    int64_t pieces = t >= want_blocks ? 1 : (want_blocks + t - 1) / t;
+    int64_t n = (nvec + pieces - 1) / pieces;
+    n = (n + 63) / 64 * 64;
+    if (n > kCombineMaxThreads) n = kCombineMaxThreads;
+    if (n < 64) n = 64;
+    *threads = static_cast<int32_t>(n);
+    *splits = static_cast<int32_t>((nvec + n - 1) / n);
 }
 
 hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *w,
@@ -166,19 +185,17 @@ hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *
 
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
                           const float *w, uint16_t *out, hipStream_t stream) {
-    int32_t splits, vpt;
-    copy_grid(c.T, c.nvec, &splits, &vpt);
-    CopyParams p = c;
-    p.vpt = vpt;
+    int32_t splits, threads;
+    combine_grid(c.T, c.nvec, &splits, &threads);
     dim3 grid(c.T, splits);
     if (c.K <= 1) {
-        combine_kernel<1><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+        combine_kernel<1><<<grid, threads, 0, stream>>>(c, y, slot, w, out);
     } else if (c.K <= 2) {
-        combine_kernel<2><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+        combine_kernel<2><<<grid, threads, 0, stream>>>(c, y, slot, w, out);
     } else if (c.K <= 4) {
-        combine_kernel<4><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+        combine_kernel<4><<<grid, threads, 0, stream>>>(c, y, slot, w, out);
     } else {
-        combine_kernel<8><<<grid, kCopyThreads, 0, stream>>>(p, y, slot, w, out);
+        combine_kernel<8><<<grid, threads, 0, stream>>>(c, y, slot, w, out);
     }
     return hipGetLastError();
 }

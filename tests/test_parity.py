@@ -147,8 +147,11 @@ def test_unit_weight_combine_of_dispatch_is_x_times_k(ep):
     out = torch.empty_like(d_x)
     ep.ep_combine(p, recv, bufs.token_slot, None, out)
     torch.cuda.synchronize()
-    xk = (d_x.view(torch.bfloat16).float() * wl.K).to(torch.bfloat16).view(torch.int16)
-    assert torch.equal(out, xk)
+    # K is a power of two, so every partial sum is exact and out == K*x as
+    # values.  Sums start from +0, so an all -0 column gives +0: compare
+    # values (-0 == +0), not bit patterns.
+    xk = (d_x.view(torch.bfloat16).float() * wl.K).to(torch.bfloat16)
+    assert torch.equal(out.view(torch.bfloat16).float(), xk.float())
 
 
 # --------------------------------------------------------------- edge cases
