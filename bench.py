@@ -74,6 +74,52 @@ def measured_traffic(workload, kernel):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
+def _counter_kib(path):
+    """Mean counter value (KiB) per kernel family in a rocprofv3 --pmc CSV."""
+    import csv
+
+    fam = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            key = ("dispatch" if "dispatch_kernel" in name else
+                   "combine" if "combine_kernel" in name else
+                   "layout" if "layout_" in name else
+                   "copy" if "copyBuffer" in name else None)
+            if key is None:
+                continue
+            fam.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            fam[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return fam
+
+
+def write_traffic(workload, fetch_csv, write_csv, fetch_copy_csv, write_copy_csv,
+                  copy_bytes=1 << 30):
+    """Turn two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then
+    WRITE_SIZE) and the same two counters on the --copy-probe run (a device
+    copy of `copy_bytes`) into HBM bytes per launch, scaled so the copy reads
+    and writes exactly `copy_bytes`.  Writes profiles/traffic.json."""
+    fetch, write = _counter_kib(fetch_csv), _counter_kib(write_csv)
+    fcopy, wcopy = _counter_kib(fetch_copy_csv), _counter_kib(write_copy_csv)
+    big = lambda d: max(d["copy"].values())      # the 1 GiB copy, not small staging copies
+    f_fetch = copy_bytes / (big(fcopy) * 1024)
+    f_write = copy_bytes / (big(wcopy) * 1024)
+    per_kernel = {}
+    for k in ("layout", "dispatch", "combine"):
+        # layout is three launches per step: sum per step (dispatch ids in order)
+        fv, wv = list(fetch[k].values()), list(write[k].values())
+        n_per_step = 3 if k == "layout" and len(fv) % 3 == 0 and len(fv) > 3 else 1
+        fk = sum(fv) / (len(fv) / n_per_step)
+        wk = sum(wv) / (len(wv) / n_per_step)
+        per_kernel[k] = {"fetch_kib": fk, "write_kib": wk,
+                         "bytes_per_launch": (fk * f_fetch + wk * f_write) * 1024}
+    rec = {"source_hash": kernel_source_hash(), "factor_fetch": f_fetch, "factor_write": f_write,
+           "copy_bytes": copy_bytes, "workloads": {workload: per_kernel}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def cpu_baseline(wl, inp, S, budget_s=12.0):
     """Time the CPU oracle (single-threaded C) on whole steps of the workload
     until about `budget_s` seconds have passed (at least one step)."""
@@ -125,7 +171,13 @@ def main():
     ap.add_argument("--workload", default="prefill4k", choices=sorted(ep_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COPY_CSV", "WRITE_COPY_CSV"),
+                    help="build profiles/traffic.json from rocprofv3 --pmc counter CSVs (no GPU needed)")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        print(json.dumps(write_traffic(args.workload, *args.write_traffic), indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the hot path; --gpus {args.gpus} is not "
@@ -148,11 +200,9 @@ def main():
 
     wl = ep_inputs.WORKLOADS[args.workload]
     inp = ep_inputs.make_inputs(wl)
-    S = oracle_free_stride = None
     p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, wl.A, 1)
     S = ep.ep_rank_stride_hint(p)        # worst-case symmetric slice, as a real buffer is sized
     p.rank_stride_rows = S
-    del oracle_free_stride
 
     dev = torch.device("cuda:0")
     d_idx = torch.from_numpy(inp.topk_idx).to(dev)
@@ -185,17 +235,28 @@ def main():
     if status != ep.EP_OK:
         raise RuntimeError(f"layout status {ep.error_string(status)}")
 
-    # timed region: exactly `steps` steps, with per-phase HIP events on the
-    # stream the kernels are launched on
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: exactly `steps` steps between two HIP events on the stream
+    # the kernels run on (no events inside: each extra event record leaves the
+    # GPU idle for a few microseconds)
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
+    e_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_step = e_start.elapsed_time(e_end) / args.steps
+
+    # per-kernel durations: the same steps again, each phase bracketed by HIP
+    # events on the same stream
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_total = events[0][0].elapsed_time(events[-1][3])
-    ms_step = ms_total / args.steps
     phase_ms = {
         "layout": float(np.mean([e[0].elapsed_time(e[1]) for e in events])),
         "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
@@ -226,6 +287,7 @@ def main():
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
         "us_per_phase": {k: v * 1e3 for k, v in phase_ms.items()},
+        "us_per_phase_note": "separate pass of the same steps with an event pair around each call",
         "us_per_step": ms_step * 1e3,
         "wall_s_timed": t_wall,
         "roofline": {
