@@ -12,40 +12,52 @@
 // order; LDS atomics only form counts, and positions come from a two-pass
 // scan plus a wave64 ballot match inside each 64-entry step.
 //
-// Multi-chunk path (three launches):
-//   1. count: one workgroup per chunk of entries builds an LDS histogram of
-//      [experts | ranks | groups | bad ids] and writes one table row;
-//   2. scan:  per 64-column tile, 16 waves split the chunk rows, sum them,
-//      combine partial sums in LDS and rewrite the table in place as
-//      exclusive per-chunk bases; column totals go to the count outputs;
-//   3. assign: one workgroup per chunk derives the expert offsets from the
-//      totals (wave scan), splits the chunk over its four waves with per-wave
-//      expert histograms, seeds one LDS cursor per (wave, expert) with
-//      offset + chunk base + earlier waves' counts, and each wave walks its
-//      part in 64-entry steps.
-// Single-chunk path (one launch): the same steps inside one workgroup, with
-// the histogram itself as the totals.
+// Entries are processed in chunks of kChunkEntries.
+// Multi-chunk path (two or three launches):
+//   1. count:  one workgroup per chunk builds an LDS histogram of
+//      [experts | ranks | groups | bad ids], writes the chunk's rows of
+//      is_token_in_rank and one row of the chunk table;
+//   2. scan:   per 64-column tile, 16 waves split the chunk rows, keep them in
+//      registers, combine partial sums in LDS and rewrite the table in place
+//      as exclusive per-chunk bases; column totals go to the count outputs;
+//   3. assign: one workgroup of W waves per chunk derives the expert offsets
+//      from the totals (a workgroup scan built on DPP wave scans), counts each wave's share of the
+//      chunk per expert, seeds one LDS cursor per (wave, expert) with offset +
+//      chunk base + earlier waves' counts, and each wave walks its share in
+//      64-entry steps.  W is 16 when E <= 512, so a full chunk is one step
+//      per wave.  When the table is small (chunks x experts per thread <=
+//      kMaxTableSum) each assign workgroup sums the table rows it needs
+//      itself and pass 2 is skipped.
+// Single-chunk path (one launch, batches of up to kChunkEntries entries): the
+// assign workgroup also builds the histogram and writes the counts.
+//
 // Every global read a step needs is issued as one batch of independent loads
-// (indices clamped into range, selects instead of branches), so each step
-// costs about one memory round trip.
+// (indices clamped into range, a buffer load's range check where a predicate
+// is needed), so each step costs about one memory round trip.
 #include "../../include/ep_get.h"
 #include "ep_internal.h"
 
 namespace epget {
 namespace {
 
-constexpr int kThreads = 256;                           // count and assign kernels
-constexpr int kWaves = kThreads / 64;
-constexpr int kIdsPerThread = kChunkEntries / kThreads;  // ids each thread loads
-constexpr int kMaxExpertsPerThread = EP_MAX_EXPERTS / kThreads;
+constexpr int kCountThreads = 256;
 constexpr int kScanWaves = 16;
-constexpr int kScanPerWave = 8;                         // chunk rows per wave per round
+constexpr int kScanPerWave = 8;  // chunk rows per wave per round
+
+// Entries in LDS are packed after the entry pass: (rank << 12) | expert for a
+// valid id (expert < 4096, rank < 1024), -1 for an empty or invalid one.
+constexpr int kRankShift = 12;
+constexpr int kExpertMask = (1 << kRankShift) - 1;
 
 __device__ __forceinline__ bool valid_id(int32_t e, int32_t E) {
     return static_cast<uint32_t>(e) < static_cast<uint32_t>(E);
 }
 
-__device__ __forceinline__ int32_t align_up(int32_t v, int32_t a) { return (v + a - 1) / a * a; }
+// Round v up to a multiple of a; a mask when a is a power of two (the usual
+// alignment), a division otherwise.
+__device__ __forceinline__ int32_t align_up(int32_t v, int32_t a) {
+    return (a & (a - 1)) == 0 ? (v + a - 1) & ~(a - 1) : (v + a - 1) / a * a;
+}
 
 // Raw buffer view of an int32 array of n elements.  A load at an index the
 // caller marks invalid reads 0 through the hardware range check of the buffer
@@ -61,57 +73,137 @@ struct I32Buffer {
     }
 };
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP moves: shifts
+// by 1, 2, 4, 8 inside each row of 16 lanes, then the broadcasts of lane 15
+// and lane 31 into the following rows.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = __lane_id();
+    const int row_lane = lane & 15;
+    int t = __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += row_lane >= 1 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += row_lane >= 2 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += row_lane >= 4 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += row_lane >= 8 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x142, 0xF, 0xF, false);  // row_bcast:15
+    v += (lane & 31) >= 16 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x143, 0xF, 0xF, false);  // row_bcast:31
+    v += lane >= 32 ? t : 0;
+    return v;
+}
+
 // Loads the n (<= kChunkEntries) ids at src into s_idx.  Every thread issues
-// its kIdsPerThread loads back to back (indices clamped into range, so no
-// load sits behind a branch); only the LDS stores are predicated.
+// its loads back to back (indices clamped into range, so no load sits behind
+// a branch); only the LDS stores are predicated.
+template <int NT>
 __device__ __forceinline__ void load_ids(const int32_t *src, int n, int *s_idx) {
+    constexpr int kPer = kChunkEntries / NT;
     if (n <= 0) return;
-    int v[kIdsPerThread];
+    int v[kPer];
 #pragma unroll
-    for (int k = 0; k < kIdsPerThread; ++k) v[k] = src[min(static_cast<int>(threadIdx.x) + k * kThreads, n - 1)];
+    for (int k = 0; k < kPer; ++k) v[k] = src[min(static_cast<int>(threadIdx.x) + k * NT, n - 1)];
 #pragma unroll
-    for (int k = 0; k < kIdsPerThread; ++k) {
-        const int i = threadIdx.x + k * kThreads;
+    for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + k * NT;
         if (i < n) s_idx[i] = v[k];
     }
 }
 
-// Entries per wave when a chunk of n entries is split over the kWaves waves
-// (a multiple of 64, so every wave but the last walks whole 64-entry steps).
-__device__ __forceinline__ int wave_span(int n) { return (n + kWaves * 64 - 1) / (kWaves * 64) * 64; }
+// Entries per wave when n entries are split over W waves (a multiple of 64,
+// so every wave but the last walks whole 64-entry steps).
+__device__ __forceinline__ int wave_span(int n, int W) { return (n + W * 64 - 1) / (W * 64) * 64; }
 
-// Entries in LDS are packed after the first pass: (rank << 12) | expert for a
-// valid id (expert < 4096, rank < 1024), -1 for an empty or invalid one.
-constexpr int kRankShift = 12;
-constexpr int kExpertMask = (1 << kRankShift) - 1;
-
-// Histogram of a chunk (raw ids in s_idx, packed in place) into s_hist
-// columns [experts | ranks | groups | bad ids], the chunk's rows of
-// is_token_in_rank, and (if s_wave is not null) per-wave expert histograms
-// for the slot walk.  Contains barriers: call from the whole workgroup.
-__device__ void chunk_histogram(const LayoutParams &p, int t0, int t1, int *s_idx,
-                                int *s_hist, int *s_wave) {
-    const int tid = threadIdx.x;
-    const int n = (t1 - t0) * p.K;
-    const int span = wave_span(n);
+// Entry pass over the chunk's raw ids in s_idx: counts experts and bad ids
+// into s_hist (if not null), each wave's share per expert into s_wave[w*E+e]
+// (if not null), and packs every entry in place.
+template <int NT>
+__device__ void entry_pass(const LayoutParams &p, int n, int W, int *s_idx, int *s_hist, int *s_wave) {
+    const int span = wave_span(n, W);
     const int bad_col = p.E + p.R + p.G;
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = threadIdx.x; i < n; i += NT) {
         const int e = s_idx[i];
-        if (e == -1) continue;
         if (!valid_id(e, p.E)) {
-            atomicAdd(&s_hist[bad_col], 1);
+            if (e != -1 && s_hist) atomicAdd(&s_hist[bad_col], 1);
             s_idx[i] = -1;
             continue;
         }
-        atomicAdd(&s_hist[e], 1);
+        if (s_hist) atomicAdd(&s_hist[e], 1);
         if (s_wave) atomicAdd(&s_wave[(i / span) * p.E + e], 1);
         s_idx[i] = static_cast<int>(p.div_L(e) << kRankShift) | e;
     }
-    __syncthreads();
-    // token-to-rank map (one byte per (token, rank)) and unique tokens per rank
-    const int nr = (t1 - t0) * p.R;
+}
+
+// One token's row of is_token_in_rank from the bit mask of its ranks
+// (R <= 64): whole 8-byte words where the row allows, bytes otherwise.
+__device__ __forceinline__ void write_map_row(uint8_t *row, int R, uint64_t mask) {
+    int r = 0;
+    if ((reinterpret_cast<uintptr_t>(row) & 7) == 0) {
+        for (; r + 8 <= R; r += 8) {
+            uint64_t bytes = 0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) bytes |= ((mask >> (r + b)) & 1ull) << (8 * b);
+            *reinterpret_cast<uint64_t *>(row + r) = bytes;
+        }
+    }
+    for (; r < R; ++r) row[r] = static_cast<uint8_t>((mask >> r) & 1);
+}
+
+// Token pass over packed entries: the chunk's rows of is_token_in_rank and
+// unique tokens per rank and per group (added into s_hist).  With R <= 64 a
+// thread takes a whole token as a bit mask of its ranks, and per-rank /
+// per-group totals are popcounts of wave ballots; otherwise one thread per
+// (token, rank) and (token, group) pair.
+template <int NT>
+__device__ void token_pass(const LayoutParams &p, int t0, int t1, const int *s_idx, int *s_hist) {
+    const int ntok = t1 - t0;
     uint8_t *map = p.is_token_in_rank + static_cast<int64_t>(t0) * p.R;
-    for (int i = tid; i < nr; i += kThreads) {
+    if (p.R <= 64) {
+        const int lane = __lane_id();
+        const int rpg = p.ranks_per_group;
+        const uint64_t group_bits = rpg >= 64 ? ~0ull : (1ull << rpg) - 1ull;
+        for (int base = 0; base < ntok; base += NT) {
+            const int tl = base + threadIdx.x;
+            const bool act = tl < ntok;
+            uint64_t mask = 0;
+            if (act) {
+                const int *ids = s_idx + tl * p.K;
+                if ((p.K & 3) == 0) {  // 16-byte LDS reads of four entries
+                    for (int j = 0; j < p.K; j += 4) {
+                        const int4 q = *reinterpret_cast<const int4 *>(ids + j);
+                        mask |= (q.x >= 0 ? 1ull << (q.x >> kRankShift) : 0ull) |
+                                (q.y >= 0 ? 1ull << (q.y >> kRankShift) : 0ull) |
+                                (q.z >= 0 ? 1ull << (q.z >> kRankShift) : 0ull) |
+                                (q.w >= 0 ? 1ull << (q.w >> kRankShift) : 0ull);
+                    }
+                } else {
+                    for (int j = 0; j < p.K; ++j) {
+                        const int v = ids[j];
+                        if (v >= 0) mask |= 1ull << (v >> kRankShift);
+                    }
+                }
+                write_map_row(map + static_cast<int64_t>(tl) * p.R, p.R, mask);
+            }
+            // lane r collects rank r's count, lane g group g's; one LDS
+            // atomic per wave and column instead of one per ballot
+            int rank_cnt = 0, group_cnt = 0;
+            for (int r = 0; r < p.R; ++r) {
+                const int cnt = __popcll(__ballot(act && ((mask >> r) & 1)));
+                rank_cnt = lane == r ? cnt : rank_cnt;
+            }
+            for (int g = 0; g < p.G; ++g) {
+                const bool in = act && ((mask >> (g * rpg)) & group_bits) != 0;
+                const int cnt = __popcll(__ballot(in));
+                group_cnt = lane == g ? cnt : group_cnt;
+            }
+            if (lane < p.R && rank_cnt) atomicAdd(&s_hist[p.E + lane], rank_cnt);
+            if (lane < p.G && group_cnt) atomicAdd(&s_hist[p.E + p.R + lane], group_cnt);
+        }
+        return;
+    }
+    const int nr = ntok * p.R;
+    for (int i = threadIdx.x; i < nr; i += NT) {
         const int tl = p.div_R(i), r = i - tl * p.R;
         const int *ids = s_idx + tl * p.K;
         int in = 0;
@@ -119,9 +211,8 @@ __device__ void chunk_histogram(const LayoutParams &p, int t0, int t1, int *s_id
         map[i] = static_cast<uint8_t>(in);
         if (in) atomicAdd(&s_hist[p.E + r], 1);
     }
-    // unique tokens per group: ranks [g*rpg, (g+1)*rpg)
-    const int ng = (t1 - t0) * p.G;
-    for (int i = tid; i < ng; i += kThreads) {
+    const int ng = ntok * p.G;
+    for (int i = threadIdx.x; i < ng; i += NT) {
         const int tl = p.div_G(i), g = i - tl * p.G;
         const int lo = g * p.ranks_per_group, hi = lo + p.ranks_per_group;
         const int *ids = s_idx + tl * p.K;
@@ -134,42 +225,66 @@ __device__ void chunk_histogram(const LayoutParams &p, int t0, int t1, int *s_id
     }
 }
 
-// Exclusive scans over all experts of the aligned and raw counts, by one
-// wave: each lane sums a contiguous run of experts, a shuffle scan combines
-// the lanes.  s_aln and s_raw get E+1 entries (the last one is the total).
-// `counts` may be the same array as s_raw (each lane reads its run before it
-// overwrites it).
-__device__ void wave_scan_counts(const LayoutParams &p, const int *counts, int *s_aln, int *s_raw) {
-    const int lane = __lane_id();
-    const int per = (p.E + 63) / 64;
-    const int e0 = min(p.E, lane * per), e1 = min(p.E, e0 + per);
+// Exclusive scans over all experts of the aligned and raw counts by the
+// whole workgroup: thread t sums experts [t*EPT, (t+1)*EPT), a DPP wave scan
+// combines the threads of a wave, and the wave totals go through LDS.
+// s_aln and s_raw get E+1 entries (the last one is the total).  `counts` may
+// be the same LDS array as s_raw: every thread reads its experts before the
+// barrier that precedes the writes.  Contains barriers: call from the whole
+// workgroup.
+template <int NT, int EPT>
+__device__ void block_scan_counts(const LayoutParams &p, const int *counts, int *s_aln,
+                                  int *s_raw, int *s_wsum) {
+    constexpr int kWavesPerBlock = NT / 64;
+    const int lane = __lane_id(), w = threadIdx.x >> 6;
+    const int e0 = threadIdx.x * EPT;
+    int ca[EPT], cr[EPT];
     int sa = 0, sr = 0;
-    for (int e = e0; e < e1; ++e) {
-        const int c = counts[e];
-        sa += align_up(c, p.A);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int c = e0 + k < p.E ? counts[e0 + k] : 0;
+        cr[k] = c;
+        ca[k] = align_up(c, p.A);
+        sa += ca[k];
         sr += c;
     }
-    int ia = sa, ir = sr;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int ta = __shfl_up(ia, d, 64), tr = __shfl_up(ir, d, 64);
-        if (lane >= d) { ia += ta; ir += tr; }
+    const int ia = wave_inclusive_sum(sa), ir = wave_inclusive_sum(sr);
+    if (lane == 63) {
+        s_wsum[w] = ia;
+        s_wsum[kWavesPerBlock + w] = ir;
     }
-    int ea = ia - sa, er = ir - sr;
-    for (int e = e0; e < e1; ++e) {
-        const int c = counts[e];
-        s_aln[e] = ea;
-        s_raw[e] = er;
-        ea += align_up(c, p.A);
-        er += c;
+    __syncthreads();
+    int pa = 0, pr = 0, ta = 0, tr = 0;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        const int a = s_wsum[i], r = s_wsum[kWavesPerBlock + i];
+        pa += i < w ? a : 0;
+        pr += i < w ? r : 0;
+        ta += a;
+        tr += r;
     }
-    if (lane == 63) { s_aln[p.E] = ia; s_raw[p.E] = ir; }
+    int ea = pa + ia - sa, er = pr + ir - sr;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        if (e0 + k < p.E) {
+            s_aln[e0 + k] = ea;
+            s_raw[e0 + k] = er;
+        }
+        ea += ca[k];
+        er += cr[k];
+    }
+    if (threadIdx.x == 0) {
+        s_aln[p.E] = ta;
+        s_raw[p.E] = tr;
+    }
 }
 
 // Per-rank results from the scans: rank_row_count and the capacity check.
 // Returns nonzero if one of this thread's ranks overflows its slice.
+template <int NT>
 __device__ int finish_ranks(const LayoutParams &p, const int *s_aln, const int *s_raw) {
     int over = 0;
-    for (int r = threadIdx.x; r < p.R; r += kThreads) {
+    for (int r = threadIdx.x; r < p.R; r += NT) {
         const int lo = r * p.L, hi = lo + p.L;
         p.rank_row_count[r] = s_raw[hi] - s_raw[lo];
         over |= (s_aln[hi] - s_aln[lo]) > p.S;
@@ -182,14 +297,15 @@ __device__ __forceinline__ int32_t status_code(int bad, int over) {
 }
 
 // Slot assignment by one wave for entries [i0, i1) of the chunk (packed
-// entries in s_idx, global entry index first + i), in 64-entry steps.  s_cur[e] holds
-// the next free row of expert e inside its slice.  Within a step, lanes naming
-// the same expert are found by matching the id bit by bit with ballots; each
-// takes the cursor plus the number of matching lanes below it, and the lowest
-// of them advances the cursor.  One wave's LDS accesses complete in issue
-// order, so every lane reads the cursor before the update lands.
-__device__ void wave_assign_slots(const LayoutParams &p, int64_t first, int i0, int i1,
-                                  int *s_cur, const int *s_idx) {
+// entries in s_idx, global entry index first + i), in 64-entry steps.  The
+// wave's cursor for expert e is s_cur[e]: the next free row of e inside its
+// slice.  Within a step, lanes naming the same expert are found by
+// matching the id bit by bit with ballots; each takes the cursor plus the
+// number of matching lanes below it, and the lowest of them advances the
+// cursor.  One wave's LDS accesses complete in issue order, so every lane
+// reads the cursor before the update lands.
+__device__ __forceinline__ void wave_assign_slots(const LayoutParams &p, int64_t first, int i0,
+                                                  int i1, int *s_cur, const int *s_idx) {
     const int lane = __lane_id();
     const uint64_t lanes_below = (1ull << lane) - 1ull;
     for (int base = i0; base < i1; base += 64) {
@@ -220,19 +336,22 @@ __device__ void wave_assign_slots(const LayoutParams &p, int64_t first, int i0, 
 }
 
 // Multi-chunk pass 1: one workgroup per chunk writes its histogram row.
-__global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutParams p) {
-    extern __shared__ int smem[];
+__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(LayoutParams p) {
+    extern __shared__ __align__(16) int smem[];
     int *s_idx = smem;
     int *s_hist = smem + kChunkEntries;
     const int c = blockIdx.x;
     const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
-    load_ids(p.topk_idx + static_cast<int64_t>(t0) * p.K, (t1 - t0) * p.K, s_idx);
-    for (int i = threadIdx.x; i < p.ncols; i += kThreads) s_hist[i] = 0;
+    const int n = (t1 - t0) * p.K;
+    load_ids<kCountThreads>(p.topk_idx + static_cast<int64_t>(t0) * p.K, n, s_idx);
+    for (int i = threadIdx.x; i < p.ncols; i += kCountThreads) s_hist[i] = 0;
     __syncthreads();
-    chunk_histogram(p, t0, t1, s_idx, s_hist, nullptr);
+    entry_pass<kCountThreads>(p, n, 1, s_idx, s_hist, nullptr);
+    __syncthreads();
+    token_pass<kCountThreads>(p, t0, t1, s_idx, s_hist);
     __syncthreads();
     int32_t *row = p.table + static_cast<int64_t>(c) * p.pitch;
-    for (int i = threadIdx.x; i < p.ncols; i += kThreads) row[i] = s_hist[i];
+    for (int i = threadIdx.x; i < p.ncols; i += kCountThreads) row[i] = s_hist[i];
 }
 
 // Multi-chunk pass 2: per 64-column tile, rewrite the table in place as
@@ -284,20 +403,31 @@ __global__ __launch_bounds__(64 * kScanWaves) void layout_scan_kernel(LayoutPara
     }
 }
 
-// Slot assignment for one chunk by four waves.  kFused: the whole batch is
-// one chunk and this kernel also builds the histogram and writes the counts;
-// otherwise the counts and the chunk's bases come from passes 1 and 2.
-// Workgroup 0 writes expert_offset, rank_row_count and the status word.
+// How the assign kernel gets each expert's total and its chunk's base.
+enum AssignMode {
+    kFusedChunk = 0,   // one chunk: this kernel builds the histogram itself
+    kSumTable = 1,     // sums the count table's rows (after pass 1 only)
+    kScannedTable = 2  // reads the bases and totals pass 2 wrote
+};
+
+// Slot assignment for one chunk by W waves.  Workgroup 0 writes
+// expert_offset, rank_row_count and the status word (and, unless pass 2 ran,
+// the per-expert / per-rank / per-group counts).
 //
-// LDS: s_idx [kChunkEntries] | s_hist [pitch] (fused only) | s_raw [E+1]
-// (not fused; fused uses s_hist) | s_aln [E+1] | s_wave [kWaves][E].
-template <bool kFused>
-__global__ __launch_bounds__(kThreads) void layout_assign_kernel(LayoutParams p) {
-    extern __shared__ int smem[];
+// LDS: s_idx [kChunkEntries] | fused: s_hist [pitch], whose expert columns
+// later hold the raw scan; otherwise s_raw [E+1] | s_aln [E+1] | s_wave [W*E].
+template <int W, int kMode>
+__global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
+    constexpr bool kFused = kMode == kFusedChunk;
+    constexpr int NT = 64 * W;
+    constexpr int kMaxExperts = W >= 16 ? 512 : (W >= 8 ? 1024 : EP_MAX_EXPERTS);
+    constexpr int kEPT = (kMaxExperts + NT - 1) / NT;  // experts per thread
+    extern __shared__ __align__(16) int smem[];
     __shared__ int s_over;
+    __shared__ int s_wsum[2 * W];
     int *s_idx = smem;
     int *s_hist = s_idx + kChunkEntries;
-    int *s_raw = s_hist;  // fused: the histogram's expert columns become the raw scan
+    int *s_raw = s_hist;
     int *s_aln = s_raw + (kFused ? p.pitch : p.E + 1);
     int *s_wave = s_aln + (p.E + 1);
     const int tid = threadIdx.x, w = tid >> 6;
@@ -307,49 +437,94 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(LayoutParams p)
     const int64_t first = static_cast<int64_t>(t0) * p.K;
 
     // 1. ids, (unfused) counts and this chunk's bases; clear the histograms
-    load_ids(p.topk_idx + first, n, s_idx);
-    int base[kMaxExpertsPerThread];
-    if (!kFused) {
+    load_ids<NT>(p.topk_idx + first, n, s_idx);
+    int base[kEPT];
+    int bad = 0;
+    if (kMode == kScannedTable) {
         const int32_t *row = p.table + static_cast<int64_t>(c) * p.pitch;
-        int cnt[kMaxExpertsPerThread];
+        int cnt[kEPT];
 #pragma unroll
-        for (int k = 0; k < kMaxExpertsPerThread; ++k) {
-            const int e = min(tid + k * kThreads, p.E - 1);
+        for (int k = 0; k < kEPT; ++k) {
+            const int e = min(tid + k * NT, p.E - 1);
             cnt[k] = p.expert_count[e];
             base[k] = row[e];
         }
 #pragma unroll
-        for (int k = 0; k < kMaxExpertsPerThread; ++k) {
-            const int e = tid + k * kThreads;
+        for (int k = 0; k < kEPT; ++k) {
+            const int e = tid + k * NT;
             if (e < p.E) s_raw[e] = cnt[k];
+        }
+        bad = p.totals[p.E + p.R + p.G];
+    } else if (kMode == kSumTable) {
+        // Column e of the table: its total over all chunks and its sum over
+        // the chunks before this one, kSumBatch rows per load batch (buffer
+        // loads return 0 past the last row).
+        constexpr int kSumBatch = 32;
+        const I32Buffer table(p.table, static_cast<uint32_t>(p.nchunks) * p.pitch);
+#pragma unroll
+        for (int k = 0; k < kEPT; ++k) {
+            const int e = tid + k * NT;
+            int tot = 0, pre = 0;
+            for (int c0 = 0; c0 < p.nchunks; c0 += kSumBatch) {
+                int v[kSumBatch];
+#pragma unroll
+                for (int q = 0; q < kSumBatch; ++q)
+                    v[q] = table.load(static_cast<uint32_t>(c0 + q) * p.pitch + e,
+                                      e < p.E && c0 + q < p.nchunks);
+#pragma unroll
+                for (int q = 0; q < kSumBatch; ++q) {
+                    tot += v[q];
+                    pre += c0 + q < c ? v[q] : 0;
+                }
+            }
+            base[k] = pre;
+            if (e < p.E) {
+                s_raw[e] = tot;
+                if (c == 0) p.expert_count[e] = tot;
+            }
+        }
+        // rank, group and bad-id columns: workgroup 0 writes their totals,
+        // and every workgroup needs the bad-id total for the status
+        for (int col = p.E + tid; col < p.ncols; col += NT) {
+            if (c != 0 && col != p.ncols - 1) continue;
+            int tot = 0;
+            for (int c0 = 0; c0 < p.nchunks; c0 += kSumBatch) {
+                int v[kSumBatch];
+#pragma unroll
+                for (int q = 0; q < kSumBatch; ++q)
+                    v[q] = table.load(static_cast<uint32_t>(c0 + q) * p.pitch + col, c0 + q < p.nchunks);
+#pragma unroll
+                for (int q = 0; q < kSumBatch; ++q) tot += v[q];
+            }
+            if (col == p.ncols - 1) {
+                s_over = tot;  // bad-id total, read back below
+            } else if (col < p.E + p.R) {
+                p.rank_token_count[col - p.E] = tot;
+            } else if (p.group_token_count) {
+                p.group_token_count[col - p.E - p.R] = tot;
+            }
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < kMaxExpertsPerThread; ++k) base[k] = 0;
-        for (int i = tid; i < p.ncols; i += kThreads) s_hist[i] = 0;
+        for (int k = 0; k < kEPT; ++k) base[k] = 0;
+        for (int i = tid; i < p.ncols; i += NT) s_hist[i] = 0;
     }
-    for (int i = tid; i < kWaves * p.E; i += kThreads) s_wave[i] = 0;
-    if (tid == 0) s_over = 0;
+    for (int i = tid; i < W * p.E; i += NT) s_wave[i] = 0;
+    if (kMode != kSumTable && tid == 0) s_over = 0;
     __syncthreads();
+    if (kMode == kSumTable) {
+        bad = s_over;
+        __syncthreads();  // s_over is reused as the capacity flag
+        if (tid == 0) s_over = 0;
+    }
 
-    // 2. histograms (fused: all columns; always: per-wave expert counts)
-    if (kFused) {
-        chunk_histogram(p, t0, t1, s_idx, s_hist, s_wave);
-    } else {
-        const int span = wave_span(n);
-        for (int i = tid; i < n; i += kThreads) {
-            const int e = s_idx[i];
-            if (valid_id(e, p.E)) {
-                atomicAdd(&s_wave[(i / span) * p.E + e], 1);
-                s_idx[i] = static_cast<int>(p.div_L(e) << kRankShift) | e;
-            } else {
-                s_idx[i] = -1;
-            }
-        }
-    }
+    // 2. per-wave expert counts (and, fused, the whole histogram)
+    entry_pass<NT>(p, n, W, s_idx, kFused ? s_hist : nullptr, s_wave);
     __syncthreads();
     if (kFused) {
-        for (int i = tid; i < p.E + p.R + p.G; i += kThreads) {
+        token_pass<NT>(p, t0, t1, s_idx, s_hist);
+        __syncthreads();
+        for (int i = tid; i < p.E + p.R + p.G; i += NT) {
             const int v = s_hist[i];
             if (i < p.E) {
                 p.expert_count[i] = v;
@@ -359,34 +534,66 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(LayoutParams p)
                 p.group_token_count[i - p.E - p.R] = v;
             }
         }
-        __syncthreads();  // s_hist's expert part becomes s_raw below
+        __syncthreads();  // s_hist's expert columns become s_raw below
     }
-    const int bad = kFused ? s_hist[p.E + p.R + p.G] : p.totals[p.E + p.R + p.G];
-    if (tid < 64) wave_scan_counts(p, s_raw, s_aln, s_raw);
+    if (kFused) bad = s_hist[p.E + p.R + p.G];
+    block_scan_counts<NT, kEPT>(p, s_raw, s_aln, s_raw, s_wsum);
     __syncthreads();
 
-    // 3. cursors: offset + chunk base, then per-wave bases inside the chunk
+    // 3. cursors: offset + chunk base, then each wave's base inside the chunk
 #pragma unroll
-    for (int k = 0; k < kMaxExpertsPerThread; ++k) {
-        const int e = tid + k * kThreads;
+    for (int k = 0; k < kEPT; ++k) {
+        const int e = tid + k * NT;
         if (e < p.E) {
             const int off = s_aln[e] - s_aln[p.div_L(e) * p.L];
+            int h[W];
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) h[ww] = s_wave[ww * p.E + e];
             int b = off + base[k];
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const int h = s_wave[ww * p.E + e];
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) {
                 s_wave[ww * p.E + e] = b;
-                b += h;
+                b += h[ww];
             }
             if (c == 0) p.expert_offset[e] = off;
         }
     }
-    if (c == 0 && finish_ranks(p, s_aln, s_raw)) atomicOr(&s_over, 1);
+    if (c == 0 && finish_ranks<NT>(p, s_aln, s_raw)) atomicOr(&s_over, 1);
     __syncthreads();
     if (c == 0 && tid == 0) *p.status = status_code(bad > 0, s_over);
 
-    // 4. each wave walks its part of the chunk
-    const int span = wave_span(n);
+    // 4. each wave walks its share of the chunk
+    const int span = wave_span(n, W);
     wave_assign_slots(p, first, min(n, w * span), min(n, (w + 1) * span), s_wave + w * p.E, s_idx);
+}
+
+// Largest table sum (rows x experts per thread) the assign kernel does itself
+// instead of running pass 2.
+constexpr int kMaxTableSum = 64;
+
+template <int W>
+hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
+    const size_t tail = sizeof(int) * ((p.E + 1) + static_cast<size_t>(W) * p.E);
+    constexpr int kEPT = ((W >= 16 ? 512 : (W >= 8 ? 1024 : EP_MAX_EXPERTS)) + 64 * W - 1) / (64 * W);
+    if (p.nchunks == 1) {
+        const size_t lds = sizeof(int) * (kChunkEntries + p.pitch) + tail;
+        layout_assign_kernel<W, kFusedChunk><<<1, 64 * W, lds, stream>>>(p);
+        return hipGetLastError();
+    }
+    const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch);
+    layout_count_kernel<<<p.nchunks, kCountThreads, lds_count, stream>>>(p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const size_t lds = sizeof(int) * (kChunkEntries + (p.E + 1)) + tail;
+    if (static_cast<int64_t>(p.nchunks) * kEPT <= kMaxTableSum) {
+        layout_assign_kernel<W, kSumTable><<<p.nchunks, 64 * W, lds, stream>>>(p);
+        return hipGetLastError();
+    }
+    layout_scan_kernel<<<p.pitch / 64, 64 * kScanWaves, 0, stream>>>(p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    layout_assign_kernel<W, kScannedTable><<<p.nchunks, 64 * W, lds, stream>>>(p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -405,22 +612,11 @@ WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t R, int32_t G) {
 }
 
 hipError_t launch_layout(const LayoutParams &p, hipStream_t stream) {
-    const size_t lds_assign_tail = sizeof(int) * ((p.E + 1) + kWaves * p.E);
-    if (p.nchunks == 1) {
-        const size_t lds = sizeof(int) * (kChunkEntries + p.pitch) + lds_assign_tail;
-        layout_assign_kernel<true><<<1, kThreads, lds, stream>>>(p);
-        return hipGetLastError();
-    }
-    const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch);
-    layout_count_kernel<<<p.nchunks, kThreads, lds_count, stream>>>(p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    layout_scan_kernel<<<p.pitch / 64, 64 * kScanWaves, 0, stream>>>(p);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const size_t lds = sizeof(int) * (kChunkEntries + (p.E + 1)) + lds_assign_tail;
-    layout_assign_kernel<false><<<p.nchunks, kThreads, lds, stream>>>(p);
-    return hipGetLastError();
+    // Walking waves per chunk: as many as the per-(wave, expert) cursors
+    // allow within 64 KB of LDS.
+    if (p.E <= 512) return launch_assign<16>(p, stream);
+    if (p.E <= 1024) return launch_assign<8>(p, stream);
+    return launch_assign<4>(p, stream);
 }
 
 }  // namespace epget
