@@ -26,7 +26,7 @@ EP_MAX_TOPK = 32
 
 # Every function the C header declares, checked by the test-suite.
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_read_status", "ep_error_string")
+           "ep_combine", "ep_combine_topk_weights", "ep_read_status", "ep_error_string")
 
 
 class EpError(RuntimeError):
@@ -76,11 +76,13 @@ def load():
         lib.ep_rank_stride_hint.restype = ctypes.c_int64
         lib.ep_rank_stride_hint.argtypes = [P]
         lib.ep_get_layout.restype = ctypes.c_int
-        lib.ep_get_layout.argtypes = [P] + [vp] * 9 + [sz, vp]
+        lib.ep_get_layout.argtypes = [P] + [vp] * 10 + [sz, vp]
         lib.ep_dispatch.restype = ctypes.c_int
         lib.ep_dispatch.argtypes = [P] + [vp] * 6 + [vp]
         lib.ep_combine.restype = ctypes.c_int
         lib.ep_combine.argtypes = [P] + [vp] * 4 + [vp]
+        lib.ep_combine_topk_weights.restype = ctypes.c_int
+        lib.ep_combine_topk_weights.argtypes = [P] + [vp] * 3 + [vp]
         lib.ep_read_status.restype = ctypes.c_int
         lib.ep_read_status.argtypes = [vp, vp]
         lib.ep_error_string.restype = ctypes.c_char_p
@@ -127,13 +129,14 @@ def ep_rank_stride_hint(problem: Problem) -> int:
 
 def ep_get_layout(problem, topk_idx, expert_count, expert_offset, rank_row_count,
                   rank_token_count, group_token_count, is_token_in_rank, token_slot,
-                  workspace, workspace_bytes=None, stream=None) -> int:
+                  cumulative_expert_recv, workspace, workspace_bytes=None, stream=None) -> int:
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     rc = load().ep_get_layout(ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
                               _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
                               _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
-                              _ptr(workspace), workspace_bytes, _stream(stream))
+                              _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
+                              _stream(stream))
     return _check(rc, "ep_get_layout")
 
 
@@ -148,6 +151,13 @@ def ep_combine(problem, y, token_slot, topk_weights, out, stream=None) -> int:
     rc = load().ep_combine(ctypes.byref(problem), _ptr(y), _ptr(token_slot), _ptr(topk_weights),
                            _ptr(out), _stream(stream))
     return _check(rc, "ep_combine")
+
+
+def ep_combine_topk_weights(problem, recv_weight, token_slot, combined_topk_weights,
+                            stream=None) -> int:
+    rc = load().ep_combine_topk_weights(ctypes.byref(problem), _ptr(recv_weight), _ptr(token_slot),
+                                        _ptr(combined_topk_weights), _stream(stream))
+    return _check(rc, "ep_combine_topk_weights")
 
 
 def ep_read_status(workspace, stream=None) -> int:

@@ -18,15 +18,18 @@ class LayoutBuffers:
     is_token_in_rank: torch.Tensor   # [T,R] uint8
     token_slot: torch.Tensor         # [T,K] int32
     workspace: torch.Tensor          # uint8, 256-byte aligned (torch allocations are)
+    cumulative_expert_recv: torch.Tensor | None = None  # [E] int64, or None
 
     def args(self):
         """Positional output arguments of ep_get_layout, in order."""
         return (self.expert_count, self.expert_offset, self.rank_row_count,
                 self.rank_token_count, self.group_token_count, self.is_token_in_rank,
-                self.token_slot, self.workspace)
+                self.token_slot, self.cumulative_expert_recv, self.workspace)
 
 
-def alloc_layout(problem: Problem, device="cuda") -> LayoutBuffers:
+def alloc_layout(problem: Problem, device="cuda", cumulative: bool = False) -> LayoutBuffers:
+    """Output buffers for ep_get_layout; `cumulative` adds a zeroed int64 [E]
+    per-expert receive counter."""
     nbytes = ep_workspace_bytes(problem)
     if nbytes == 0:
         raise ValueError("invalid ep_problem")
@@ -42,4 +45,5 @@ def alloc_layout(problem: Problem, device="cuda") -> LayoutBuffers:
         is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=device),
         token_slot=torch.empty((T, K), **i32),
         workspace=torch.empty(nbytes, dtype=torch.uint8, device=device),
+        cumulative_expert_recv=torch.zeros(E, dtype=torch.int64, device=device) if cumulative else None,
     )

@@ -79,7 +79,8 @@ int64_t ep_rank_stride_hint(const ep_problem *p) {
 int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
                   int32_t *expert_offset, int32_t *rank_row_count, int32_t *rank_token_count,
                   int32_t *group_token_count, uint8_t *is_token_in_rank, int32_t *token_slot,
-                  void *workspace, size_t workspace_bytes, void *stream) {
+                  int64_t *cumulative_expert_recv, void *workspace, size_t workspace_bytes,
+                  void *stream) {
     int rc = check_problem(p);
     if (rc != EP_OK) return rc;
     const bool has_tokens = p->num_tokens > 0;
@@ -88,7 +89,8 @@ int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
     if (has_tokens && (!topk_idx || !is_token_in_rank || !token_slot)) return EP_ERR_INVALID_ARG;
     if (!aligned(topk_idx, 4) || !aligned(expert_count, 4) || !aligned(expert_offset, 4) ||
         !aligned(rank_row_count, 4) || !aligned(rank_token_count, 4) ||
-        !aligned(group_token_count, 4) || !aligned(token_slot, 4) || !aligned(workspace, 256))
+        !aligned(group_token_count, 4) || !aligned(token_slot, 4) ||
+        !aligned(cumulative_expert_recv, 8) || !aligned(workspace, 256))
         return EP_ERR_INVALID_ARG;
     const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts,
                                         p->num_ranks, p->num_groups);
@@ -122,6 +124,7 @@ int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
     lp.group_token_count = group_token_count;
     lp.is_token_in_rank = is_token_in_rank;
     lp.token_slot = token_slot;
+    lp.cumulative = cumulative_expert_recv;
     char *ws = static_cast<char *>(workspace);
     lp.status = reinterpret_cast<int32_t *>(ws);
     lp.totals = reinterpret_cast<int32_t *>(ws + w.totals_off);
@@ -155,6 +158,20 @@ int ep_combine(const ep_problem *p, const uint16_t *y, const int32_t *token_slot
         return EP_ERR_INVALID_ARG;
     return hip_rc(epget::launch_combine(copy_params(p), y, token_slot, topk_weights, out,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_topk_weights(const ep_problem *p, const float *recv_weight,
+                            const int32_t *token_slot, float *combined_topk_weights,
+                            void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!recv_weight || !token_slot || !combined_topk_weights) return EP_ERR_INVALID_ARG;
+    if (!aligned(recv_weight, 4) || !aligned(token_slot, 4) || !aligned(combined_topk_weights, 4))
+        return EP_ERR_INVALID_ARG;
+    return hip_rc(epget::launch_combine_weights(copy_params(p), recv_weight, token_slot,
+                                                combined_topk_weights,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int ep_read_status(const void *workspace, void *stream) {

@@ -51,6 +51,7 @@ struct LayoutParams {
     int32_t *group_token_count;  // may be null
     uint8_t *is_token_in_rank;
     int32_t *token_slot;
+    int64_t *cumulative;  // may be null
     int32_t *status, *totals, *table;
 };
 
@@ -71,6 +72,8 @@ hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *
                            float *recv_w, hipStream_t stream);
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
                           const float *w, uint16_t *out, hipStream_t stream);
+hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, const int32_t *slot,
+                                  float *combined_w, hipStream_t stream);
 
 // Grid shape for the row kernels: (tokens, column splits) and vectors per
 // thread, chosen so that small batches still spread over all CUs.

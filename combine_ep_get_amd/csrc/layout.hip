@@ -452,7 +452,10 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
 #pragma unroll
         for (int k = 0; k < kEPT; ++k) {
             const int e = tid + k * NT;
-            if (e < p.E) s_raw[e] = cnt[k];
+            if (e < p.E) {
+                s_raw[e] = cnt[k];
+                if (c == 0 && p.cumulative) p.cumulative[e] += cnt[k];
+            }
         }
         bad = p.totals[p.E + p.R + p.G];
     } else if (kMode == kSumTable) {
@@ -480,7 +483,10 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
             base[k] = pre;
             if (e < p.E) {
                 s_raw[e] = tot;
-                if (c == 0) p.expert_count[e] = tot;
+                if (c == 0) {
+                    p.expert_count[e] = tot;
+                    if (p.cumulative) p.cumulative[e] += tot;
+                }
             }
         }
         // rank, group and bad-id columns: workgroup 0 writes their totals,
@@ -528,6 +534,7 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
             const int v = s_hist[i];
             if (i < p.E) {
                 p.expert_count[i] = v;
+                if (p.cumulative) p.cumulative[i] += v;
             } else if (i < p.E + p.R) {
                 p.rank_token_count[i - p.E] = v;
             } else if (p.group_token_count) {

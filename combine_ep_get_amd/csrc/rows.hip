@@ -125,6 +125,16 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     }
 }
 
+// combined_topk_weights: one thread per (token, top-k) entry.
+__global__ __launch_bounds__(256) void combine_weights_kernel(CopyParams c, const float *__restrict__ recv_w,
+                                                              const int32_t *__restrict__ slot,
+                                                              float *__restrict__ combined_w) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= static_cast<int64_t>(c.T) * c.K) return;
+    const int32_t s = slot[i];
+    combined_w[i] = slot_ok(s, c.num_rows) ? recv_w[s] : 0.0f;
+}
+
 }  // namespace
 
 void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt) {
@@ -197,6 +207,13 @@ hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t 
     } else {
         combine_kernel<8><<<grid, threads, 0, stream>>>(c, y, slot, w, out);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, const int32_t *slot,
+                                  float *combined_w, hipStream_t stream) {
+    const int64_t n = static_cast<int64_t>(c.T) * c.K;
+    combine_weights_kernel<<<(n + 255) / 256, 256, 0, stream>>>(c, recv_w, slot, combined_w);
     return hipGetLastError();
 }
 

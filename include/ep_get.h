@@ -120,6 +120,13 @@ int64_t ep_rank_stride_hint(const ep_problem *problem);
  *                                empty or invalid ids and for rows at or past
  *                                S inside their slice.  This is the handle
  *                                ep_dispatch and ep_combine take ([SYM] §9.2).
+ *                                Reusing it for later dispatch/combine calls
+ *                                without a new layout is the cached mode of
+ *                                [SYM] §6.1 (cached_mode).
+ *   cumulative_expert_recv [E] int64, or NULL: expert_count is added to it
+ *                                (the cumulative per-expert receive
+ *                                statistics of [SYM] §6.1); the caller
+ *                                zeroes it once.  8-byte aligned.
  *   workspace         ep_workspace_bytes(problem) bytes, device.
  * Device-detected errors (read with ep_read_status): an id outside [0,E)
  * other than -1 gives EP_ERR_BAD_EXPERT and is treated as empty; a rank whose
@@ -130,8 +137,8 @@ int ep_get_layout(const ep_problem *problem, const int32_t *topk_idx,
                   int32_t *expert_count, int32_t *expert_offset,
                   int32_t *rank_row_count, int32_t *rank_token_count,
                   int32_t *group_token_count, uint8_t *is_token_in_rank,
-                  int32_t *token_slot, void *workspace, size_t workspace_bytes,
-                  void *stream);
+                  int32_t *token_slot, int64_t *cumulative_expert_recv,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Dispatch: recv_x[token_slot[t,j], :] = x[t, :] (bit copy), plus
  * recv_src_token[slot] = t and recv_weight[slot] = topk_weights[t,j] — the
@@ -167,6 +174,19 @@ int ep_dispatch(const ep_problem *problem, const uint16_t *x,
 int ep_combine(const ep_problem *problem, const uint16_t *y,
                const int32_t *token_slot, const float *topk_weights,
                uint16_t *out, void *stream);
+
+/* Combined top-k weights: combined_topk_weights[t,j] = recv_weight[token_slot[t,j]]
+ * (0 for slots outside [0, R*S)) — the per-row weights that travelled with
+ * the dispatched rows, gathered back into token order, as combine returns
+ * combined_topk_weights beside combined_x in [SYM] §9.2.  After ep_dispatch
+ * with weights it reproduces topk_weights exactly.
+ *
+ *   recv_weight           [R*S] fp32 device (ep_dispatch's recv_weight)
+ *   token_slot            [T,K] int32 device
+ *   combined_topk_weights [T,K] fp32 device, written */
+int ep_combine_topk_weights(const ep_problem *problem, const float *recv_weight,
+                            const int32_t *token_slot, float *combined_topk_weights,
+                            void *stream);
 
 /* Synchronises `stream`, then returns the status word the last
  * ep_get_layout on that workspace wrote (EP_OK, EP_ERR_BAD_EXPERT or

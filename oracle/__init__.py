@@ -56,6 +56,16 @@ def open_library(path: str):
     lib.oracle_dispatch.argtypes = [i32, i32, i32, i64] + [vp] * 6
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [i32, i32, i32, i64] + [vp] * 4
+    lib.oracle_float_to_e4m3.restype = None
+    lib.oracle_float_to_e4m3.argtypes = [i64, vp, vp]
+    lib.oracle_e4m3_to_float.restype = None
+    lib.oracle_e4m3_to_float.argtypes = [i64, vp, vp]
+    lib.oracle_quantize_fp8.restype = None
+    lib.oracle_quantize_fp8.argtypes = [i32, i32, vp, vp, vp]
+    lib.oracle_dispatch_fp8.restype = None
+    lib.oracle_dispatch_fp8.argtypes = [i32, i32, i32, i64] + [vp] * 6 + [i64, i64, vp, vp]
+    lib.oracle_combine_topk_weights.restype = None
+    lib.oracle_combine_topk_weights.argtypes = [i32, i32, i64, vp, vp, vp]
     lib.oracle_double_to_bf16.restype = None
     lib.oracle_double_to_bf16.argtypes = [i64, vp, vp]
     lib.oracle_bf16_to_double.restype = None
@@ -186,6 +196,75 @@ def combine(y: np.ndarray, token_slot: np.ndarray, topk_weights: np.ndarray | No
     w = None if topk_weights is None else _c(topk_weights, np.float32)
     _load().oracle_combine(T, H, K, y.shape[0], _p(y), _p(slot), _p(w), _p(out))
     return out
+
+
+def combine_topk_weights(recv_weight: np.ndarray, token_slot: np.ndarray) -> np.ndarray:
+    """Per-row weights gathered back into token order ([SYM] §9.2,
+    combined_topk_weights); 0 where the slot is outside ``[0, rows)``."""
+    rw = _c(recv_weight, np.float32)
+    slot = _c(token_slot, np.int32)
+    T, K = slot.shape
+    out = np.empty((T, K), np.float32)
+    _load().oracle_combine_topk_weights(T, K, rw.shape[0], _p(rw), _p(slot), _p(out))
+    return out
+
+
+def float_to_e4m3(v: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 code (ties to even, saturating at 448) of fp32 values."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_float_to_e4m3(v.size, _p(v), _p(out))
+    return out
+
+
+def e4m3_to_float(q: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    out = np.empty(q.shape, np.float32)
+    _load().oracle_e4m3_to_float(q.size, _p(q), _p(out))
+    return out
+
+
+def quantize_fp8(x: np.ndarray):
+    """Per-token, per-128-channel e4m3 quantisation of bf16 rows: returns
+    ``(codes [T,H] uint8, scales [T,H/128] fp32)`` with sf = amax/448 and
+    codes = e4m3(x * (448/amax)) in fp32 (the reading of the FP8 dispatch
+    arguments of [SYM] §6.1; the pages give no rule)."""
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    assert H % 128 == 0
+    q = np.empty((T, H), np.uint8)
+    sf = np.empty((T, H // 128), np.float32)
+    _load().oracle_quantize_fp8(T, H, _p(x), _p(q), _p(sf))
+    return q, sf
+
+
+def dispatch_fp8(q: np.ndarray, sf: np.ndarray, token_slot: np.ndarray, num_rows: int,
+                 topk_weights: np.ndarray | None = None, column_major_sf: bool = False,
+                 sf_alignment: int = 4):
+    """FP8 dispatch ([SYM] §6.1 sf arguments, [V2] TMA-aligned column-major
+    scale layout).  Returns ``(recv_q [rows,H], recv_sf (flat), strides,
+    recv_src_token, recv_weight)``; the scale of (row, block b) is
+    ``recv_sf[row*strides[0] + b*strides[1]]``."""
+    q = _c(q, np.uint8)
+    sf = _c(sf, np.float32)
+    slot = _c(token_slot, np.int32)
+    T, H = q.shape
+    K = slot.shape[1]
+    nb = H // 128
+    if column_major_sf:
+        strides = (1, -(-num_rows // sf_alignment) * sf_alignment)
+        size = strides[1] * nb
+    else:
+        strides = (nb, 1)
+        size = num_rows * nb
+    recv_q = np.zeros((num_rows, H), np.uint8)
+    recv_sf = np.full(size, np.nan, np.float32)
+    src = np.full(num_rows, -1, np.int32)
+    rw = np.full(num_rows, np.nan, np.float32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    _load().oracle_dispatch_fp8(T, H, K, num_rows, _p(q), _p(sf), _p(w), _p(slot), _p(recv_q),
+                                _p(recv_sf), strides[0], strides[1], _p(src), _p(rw))
+    return recv_q, recv_sf, strides, src, rw
 
 
 def double_to_bf16(v: np.ndarray) -> np.ndarray:

@@ -173,6 +173,23 @@ void oracle_dispatch(int32_t T, int32_t H, int32_t K, int64_t num_rows,
     }
 }
 
+/*
+ * Combined top-k weights: the weight carried by each dispatched row, read
+ * back into token order ([SYM] §9.2: combine returns combined_topk_weights
+ * beside combined_x).  Slots < 0 or >= num_rows give 0.
+ */
+void oracle_combine_topk_weights(int32_t T, int32_t K, int64_t num_rows,
+                                 const float *recv_weight, const int32_t *token_slot,
+                                 float *combined_topk_weights)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < K; ++j) {
+            int64_t s = token_slot[t * K + j];
+            combined_topk_weights[t * K + j] = (s < 0 || s >= num_rows) ? 0.0f : recv_weight[s];
+        }
+    }
+}
+
 /* bf16 bit pattern -> value (exact). */
 static double bf16_to_double(uint16_t b)
 {
@@ -232,6 +249,111 @@ void oracle_combine(int32_t T, int32_t H, int32_t K, int64_t num_rows,
                 acc += w * bf16_to_double(y[s * H + h]);
             }
             out[t * H + h] = double_to_bf16(acc);
+        }
+    }
+}
+
+/*
+ * FP8 (e4m3, the OCP "fn" variant: 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, 0x7F/0xFF NaN, largest finite 448) dispatch support.
+ *
+ * The pages show that dispatch can move FP8 rows with scale factors ([SYM]
+ * §6.1: sf, num_sf_packs, sf_token_stride, sf_hidden_stride; §9.2:
+ * use_fp8_dispatch; [V2] elastic.py block: a TMA-aligned column-major scale
+ * layout with sf_token_stride = 1 and sf_hidden_stride = the aligned token
+ * count) but not the quantisation rule.  The reading taken: one fp32 scale
+ * per token and block of 128 channels, sf = amax / 448, codes = the nearest
+ * e4m3 value (ties to even, magnitudes above 448 saturate) of
+ * x * (448 / amax), everything in fp32; an all-zero block gets sf = 0 and
+ * zero codes.
+ */
+
+/* The e4m3 value of a non-negative code c < 0x7F. */
+static float e4m3_magnitude(int c)
+{
+    int e = c >> 3, m = c & 7;
+    if (e == 0) return ldexpf((float)m, -9);          /* subnormal: m * 2^-9 */
+    return ldexpf((float)(8 + m), e - 10);             /* (1 + m/8) * 2^(e-7) */
+}
+
+/* Nearest e4m3 code by search over the 127 finite magnitudes, ties to the
+ * even code; magnitudes above 448 saturate, NaN maps to 0x7F. */
+static uint8_t float_to_e4m3(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    float a = fabsf(v);
+    if (a >= 448.0f) return sign | 0x7E;
+    int best = 0;
+    for (int c = 1; c < 0x7F; ++c) {
+        float dc = fabsf(e4m3_magnitude(c) - a), db = fabsf(e4m3_magnitude(best) - a);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+void oracle_float_to_e4m3(int64_t n, const float *in, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = float_to_e4m3(in[i]);
+}
+
+void oracle_e4m3_to_float(int64_t n, const uint8_t *in, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        int c = in[i] & 0x7F;
+        float m = c == 0x7F ? NAN : e4m3_magnitude(c);
+        out[i] = (in[i] & 0x80) ? -m : m;
+    }
+}
+
+/* Per-token, per-128-channel quantisation of bf16 rows [T,H] (H % 128 == 0)
+ * into e4m3 codes [T,H] and fp32 scales [T, H/128] (token-major). */
+void oracle_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, float *sf)
+{
+    const int32_t nb = H / 128;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t b = 0; b < nb; ++b) {
+            const uint16_t *xb = x + t * H + (int64_t)b * 128;
+            float amax = 0.0f;
+            for (int i = 0; i < 128; ++i) {
+                uint32_t u = (uint32_t)xb[i] << 16;
+                float f;
+                memcpy(&f, &u, sizeof f);
+                if (fabsf(f) > amax) amax = fabsf(f);
+            }
+            const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+            for (int i = 0; i < 128; ++i) {
+                uint32_t u = (uint32_t)xb[i] << 16;
+                float f;
+                memcpy(&f, &u, sizeof f);
+                q[t * H + (int64_t)b * 128 + i] = float_to_e4m3(f * inv);
+            }
+            sf[t * nb + b] = amax / 448.0f;
+        }
+    }
+}
+
+/* FP8 dispatch: rows of H code bytes go where dispatch sends bf16 rows, and
+ * each received row's H/128 scales go to recv_sf[row * sf_token_stride +
+ * b * sf_hidden_stride] (token-major: strides (H/128, 1); the TMA-aligned
+ * column-major layout: (1, aligned row count)).  Source index and weight as
+ * in oracle_dispatch. */
+void oracle_dispatch_fp8(int32_t T, int32_t H, int32_t K, int64_t num_rows,
+                         const uint8_t *q, const float *sf, const float *topk_weights,
+                         const int32_t *token_slot, uint8_t *recv_q, float *recv_sf,
+                         int64_t sf_token_stride, int64_t sf_hidden_stride,
+                         int32_t *recv_src_token, float *recv_weight)
+{
+    const int32_t nb = H / 128;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < K; ++j) {
+            int64_t s = token_slot[t * K + j];
+            if (s < 0 || s >= num_rows) continue;
+            memcpy(recv_q + s * H, q + t * H, (size_t)H);
+            for (int32_t b = 0; b < nb; ++b)
+                recv_sf[s * sf_token_stride + b * sf_hidden_stride] = sf[t * nb + b];
+            if (recv_src_token) recv_src_token[s] = (int32_t)t;
+            if (recv_weight) recv_weight[s] = topk_weights ? topk_weights[t * K + j] : 1.0f;
         }
     }
 }

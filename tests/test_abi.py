@@ -59,10 +59,11 @@ def test_invalid_problems_rejected_before_launch(bad):
     lib = ep.load()
     fake = 1 << 20   # never dereferenced: validation fails first
     rc = lib.ep_get_layout(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
-                           fake, 1 << 30, None)
+                           fake, fake, 1 << 30, None)
     assert rc == ep.EP_ERR_INVALID_ARG
     assert lib.ep_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(p), fake, fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_topk_weights(ctypes.byref(p), fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_reserved_field_must_be_zero():
@@ -82,6 +83,8 @@ def test_bad_pointers_rejected():
     # workspace too small or misaligned
     need = ep.ep_workspace_bytes(p)
     args = [a] * 8
-    assert lib.ep_get_layout(ctypes.byref(p), *args, a, need - 1, None) == ep.EP_ERR_INVALID_ARG
-    assert lib.ep_get_layout(ctypes.byref(p), *args, a + 16, need, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(ctypes.byref(p), *args, None, a, need - 1, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(ctypes.byref(p), *args, None, a + 16, need, None) == ep.EP_ERR_INVALID_ARG
+    # cumulative counter must be 8-byte aligned
+    assert lib.ep_get_layout(ctypes.byref(p), *args, a + 4, a, need, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_read_status(None, None) == ep.EP_ERR_INVALID_ARG

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_fp8 as fp8pins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
@@ -29,11 +30,19 @@ MUTATIONS = {
     "weights_reversed": ("(double)topk_weights[t * K + j]", "(double)topk_weights[t * K + (K - 1 - j)]"),
     "round_by_truncation": ("rint(ldexp(a, -qexp))", "floor(ldexp(a, -qexp))"),
     "one_bit_too_many": ("int qexp = e - 8;", "int qexp = e - 9;"),
-    "src_index_is_topk_pos": ("recv_src_token[s] = (int32_t)t;", "recv_src_token[s] = (int32_t)j;"),
+    "src_index_is_topk_pos": (
+        "memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));\n            if (recv_src_token) recv_src_token[s] = (int32_t)t;",
+        "memcpy(recv_x + s * H, x + t * H, (size_t)H * sizeof(uint16_t));\n            if (recv_src_token) recv_src_token[s] = (int32_t)j;"),
     "group_range_shifted": ("for (int32_t r = g * ranks_per_group; r < (g + 1) * ranks_per_group; ++r)",
                             "for (int32_t r = g; r < g + ranks_per_group; ++r)"),
     "empty_id_counted_bad": ("if (e == -1) continue;", ""),
     "row_sum_uses_aligned": ("rows += expert_count[e];", "rows += align_up(expert_count[e], A);"),
+    "e4m3_ties_away": ("(dc == db && (c & 1) == 0)", "(dc == db)"),
+    "fp8_scale_constant": ("const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;",
+                           "const float inv = amax > 0.0f ? 240.0f / amax : 0.0f;"),
+    "fp8_scale_inverted": ("sf[t * nb + b] = amax / 448.0f;", "sf[t * nb + b] = 448.0f / amax;"),
+    "fp8_scale_strides_swapped": ("recv_sf[s * sf_token_stride + b * sf_hidden_stride]",
+                                  "recv_sf[s * sf_hidden_stride + b * sf_token_stride]"),
 }
 
 
@@ -52,6 +61,10 @@ def _pin_suite():
     pins.test_one_hot_combine_returns_x()
     pins.test_weighted_combine_matches_numpy_gather("tiny")
     pins.test_bf16_rounding_matches_torch_on_floats()
+    fp8pins.test_e4m3_rounding_matches_torch()
+    fp8pins.test_quantize_matches_restatement("tiny")
+    fp8pins.test_quantize_zero_block_and_extremes()
+    fp8pins.test_dispatch_fp8_moves_codes_and_scales(True)
 
 
 def test_unmutated_build_passes(tmp_path):

@@ -253,6 +253,21 @@ def test_dispatch_without_weights_or_maps():
     np.testing.assert_array_equal(rw[lay.token_slot.ravel()], 1.0)
 
 
+def test_combined_topk_weights_round_trip():
+    """Weights carried by the dispatched rows come back in token order."""
+    inp = ep_inputs.make_inputs("tiny")
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S)
+    _, _, rw = oracle.dispatch(inp.x, lay.token_slot, wl.R * S, inp.topk_weights)
+    np.testing.assert_array_equal(oracle.combine_topk_weights(rw, lay.token_slot), inp.topk_weights)
+    slot = lay.token_slot.copy()
+    slot[0, 1] = -1
+    slot[1, 0] = wl.R * S     # outside the buffer
+    got = oracle.combine_topk_weights(rw, slot)
+    assert got[0, 1] == 0.0 and got[1, 0] == 0.0
+
+
 # ---------------------------------------------------------------- combine
 
 def _dispatched(name):

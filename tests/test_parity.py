@@ -269,6 +269,56 @@ def test_large_expert_count_and_rank_count(ep):
     _case(ep, _route_uniform(rng, T, E, K), E, R, H=16)
 
 
+def test_cumulative_expert_counts_and_cached_layout(ep):
+    """Cumulative per-expert receive counts across calls, and dispatch/combine
+    reusing one layout (cached mode) for new activations."""
+    inp = ep_inputs.make_inputs("prefill4k")
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, 1, S)
+    bufs = ep.alloc_layout(p, cumulative=True)
+    ref = oracle.layout(inp.topk_idx, wl.E, wl.R, S)
+    idx2 = ep_inputs.make_inputs("prefill4k", seed=5, with_x=False).topk_idx
+    ref2 = oracle.layout(idx2, wl.E, wl.R, S)
+    ep.ep_get_layout(p, dev(inp.topk_idx), *bufs.args())
+    ep.ep_get_layout(p, dev(idx2), *bufs.args())
+    ep.ep_get_layout(p, dev(inp.topk_idx), *bufs.args())
+    want = 2 * ref.expert_count.astype(np.int64) + ref2.expert_count
+    np.testing.assert_array_equal(bufs.cumulative_expert_recv.cpu().numpy(), want)
+    # cached mode: the last layout serves two dispatch/combine rounds
+    rows = wl.R * S
+    recv = torch.empty((rows, wl.H), dtype=torch.int16, device="cuda")
+    rw = torch.empty(rows, dtype=torch.float32, device="cuda")
+    comb_w = torch.empty((wl.T, wl.K), dtype=torch.float32, device="cuda")
+    s = ref.token_slot.ravel()
+    for seed in (21, 22):
+        x = ep_inputs.bf16_normal(np.random.default_rng(seed), (wl.T, wl.H))
+        ep.ep_dispatch(p, bf16_dev(x), dev(inp.topk_weights), bufs.token_slot, recv, None, rw)
+        ep.ep_combine_topk_weights(p, rw, bufs.token_slot, comb_w)
+        torch.cuda.synchronize()
+        ref_rx, _, _ = oracle.dispatch(x, ref.token_slot, rows, inp.topk_weights)
+        np.testing.assert_array_equal(host_u16(recv)[s], ref_rx[s])
+        np.testing.assert_array_equal(comb_w.cpu().numpy(), inp.topk_weights)
+
+
+def test_combined_topk_weights_with_invalid_slots(ep):
+    rng = np.random.default_rng(9)
+    idx = rng.integers(0, 32, size=(1500, 4)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    E, R = 32, 4
+    counts = np.bincount(idx[idx >= 0].ravel(), minlength=E)
+    S = tight_stride(counts, E, R) - 3          # overflow: some slots become -1
+    ref = oracle.layout(idx, E, R, S)
+    assert ref.status == oracle.CAPACITY
+    p, bufs, status = gpu_layout(ep, idx, E, R, S, H=64)
+    assert_layout_matches(ep, bufs, status, ref)
+    recv_w = rng.standard_normal(R * S).astype(np.float32)
+    out = torch.empty((1500, 4), dtype=torch.float32, device="cuda")
+    ep.ep_combine_topk_weights(p, dev(recv_w), bufs.token_slot, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), oracle.combine_topk_weights(recv_w, ref.token_slot))
+
+
 def test_repeatable(ep):
     inp = ep_inputs.make_inputs("zipf8k", with_x=False)
     wl = inp.wl
