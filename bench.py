@@ -36,18 +36,24 @@ KERNEL_SOURCES = ["combine_ep_get_amd/csrc/rows.hip", "combine_ep_get_amd/csrc/l
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def algorithmic_bytes(wl, R_is_token_in_rank=True):
+def algorithmic_bytes(wl, fp8=False):
     """Bytes each kernel must move per launch (what the method itself needs).
 
     layout:   read topk_idx (4TK), write token_slot (4TK) and is_token_in_rank (TR)
     dispatch: read x (2TH), write K rows per token (2TKH); read slot and weight
-              (8TK), write source index and weight per row (8TK)
+              (8TK), write source index and weight per row (8TK).  FP8: rows
+              of H bytes plus H/128 fp32 scales per row (TH + 4T*H/128 read,
+              K times that written)
     combine:  read K rows per token (2TKH), write out (2TH); read slot and
               weight (8TK)
     """
     T, H, K, R = wl.T, wl.H, wl.K, wl.R
-    lay = 8 * T * K + (T * R if R_is_token_in_rank else 0)
-    dis = 2 * T * H + 2 * T * K * H + 16 * T * K
+    lay = 8 * T * K + T * R
+    if fp8:
+        row = H + 4 * (H // 128)
+        dis = T * row + T * K * row + 16 * T * K
+    else:
+        dis = 2 * T * H + 2 * T * K * H + 16 * T * K
     com = 2 * T * K * H + 2 * T * H + 8 * T * K
     return {"layout": lay, "dispatch": dis, "combine": com}
 
@@ -171,6 +177,8 @@ def main():
     ap.add_argument("--workload", default="prefill4k", choices=sorted(ep_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 dispatch (e4m3 rows + per-128-channel scales); combine stays bf16")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COPY_CSV", "WRITE_COPY_CSV"),
                     help="build profiles/traffic.json from rocprofv3 --pmc counter CSVs (no GPU needed)")
     args = ap.parse_args()
@@ -214,6 +222,31 @@ def main():
     recv_w = torch.empty(wl.R * S, dtype=torch.float32, device=dev)
     out = torch.empty((wl.T, wl.H), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
+    quant_us = None
+    if args.fp8:
+        # quantisation happens upstream of dispatch (in the producing layer);
+        # it is timed on its own and not part of the step
+        nsf = wl.H // 128
+        d_q = torch.empty((wl.T, wl.H), dtype=torch.uint8, device=dev)
+        d_sf = torch.empty((wl.T, nsf), dtype=torch.float32, device=dev)
+        recv_q = torch.empty((wl.R * S, wl.H), dtype=torch.uint8, device=dev)
+        recv_sf = torch.empty(wl.R * S * nsf, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ep.ep_quantize_fp8(p, d_x, d_q, d_sf, stream=stream)
+        qe0, qe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        qe0.record(stream)
+        for _ in range(20):
+            ep.ep_quantize_fp8(p, d_x, d_q, d_sf, stream=stream)
+        qe1.record(stream)
+        torch.cuda.synchronize()
+        quant_us = qe0.elapsed_time(qe1) / 20 * 1e3
+
+    def dispatch_call():
+        if args.fp8:
+            ep.ep_dispatch_fp8(p, d_q, d_sf, d_w, bufs.token_slot, recv_q, recv_sf, nsf, 1,
+                               recv_src, recv_w, stream=stream)
+        else:
+            ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, recv_src, recv_w, stream=stream)
 
     def step(ev=None):
         if ev is not None:
@@ -221,7 +254,7 @@ def main():
         ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, recv_src, recv_w, stream=stream)
+        dispatch_call()
         if ev is not None:
             ev[2].record(stream)
         ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
@@ -262,7 +295,7 @@ def main():
         "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
         "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
     }
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes(wl, fp8=args.fp8)
     total_bytes = sum(nbytes.values())
     eff_gbps = total_bytes / (ms_step * 1e-3) / 1e9
     dominant = max(("dispatch", "combine"), key=lambda k: phase_ms[k])
@@ -280,15 +313,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 dispatch, bf16 combine" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "R": wl.R,
-                   "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed},
+                   "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
+                   "dispatch": "fp8" if args.fp8 else "bf16"},
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
         "us_per_phase": {k: v * 1e3 for k, v in phase_ms.items()},
         "us_per_phase_note": "separate pass of the same steps with an event pair around each call",
         "us_per_step": ms_step * 1e3,
+        "us_quantize_fp8": quant_us,
         "wall_s_timed": t_wall,
         "roofline": {
             "kernel": dominant,
@@ -301,7 +336,7 @@ def main():
             "algorithmic_bytes": nbytes[dominant],
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8:
         result["cpu_baseline"] = cpu_baseline(wl, inp, S)
     print(json.dumps(result), flush=True)
 

@@ -26,7 +26,8 @@ EP_MAX_TOPK = 32
 
 # Every function the C header declares, checked by the test-suite.
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_combine_topk_weights", "ep_read_status", "ep_error_string")
+           "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8", "ep_combine_topk_weights",
+           "ep_read_status", "ep_error_string")
 
 
 class EpError(RuntimeError):
@@ -81,6 +82,10 @@ def load():
         lib.ep_dispatch.argtypes = [P] + [vp] * 6 + [vp]
         lib.ep_combine.restype = ctypes.c_int
         lib.ep_combine.argtypes = [P] + [vp] * 4 + [vp]
+        lib.ep_quantize_fp8.restype = ctypes.c_int
+        lib.ep_quantize_fp8.argtypes = [P] + [vp] * 3 + [vp]
+        lib.ep_dispatch_fp8.restype = ctypes.c_int
+        lib.ep_dispatch_fp8.argtypes = [P] + [vp] * 6 + [ctypes.c_int64, ctypes.c_int64] + [vp] * 2 + [vp]
         lib.ep_combine_topk_weights.restype = ctypes.c_int
         lib.ep_combine_topk_weights.argtypes = [P] + [vp] * 3 + [vp]
         lib.ep_read_status.restype = ctypes.c_int
@@ -151,6 +156,22 @@ def ep_combine(problem, y, token_slot, topk_weights, out, stream=None) -> int:
     rc = load().ep_combine(ctypes.byref(problem), _ptr(y), _ptr(token_slot), _ptr(topk_weights),
                            _ptr(out), _stream(stream))
     return _check(rc, "ep_combine")
+
+
+def ep_quantize_fp8(problem, x, x_fp8, x_sf, stream=None) -> int:
+    rc = load().ep_quantize_fp8(ctypes.byref(problem), _ptr(x), _ptr(x_fp8), _ptr(x_sf),
+                                _stream(stream))
+    return _check(rc, "ep_quantize_fp8")
+
+
+def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, recv_sf,
+                    sf_token_stride, sf_hidden_stride, recv_src_token=None, recv_weight=None,
+                    stream=None) -> int:
+    rc = load().ep_dispatch_fp8(ctypes.byref(problem), _ptr(x_fp8), _ptr(x_sf), _ptr(topk_weights),
+                                _ptr(token_slot), _ptr(recv_x_fp8), _ptr(recv_sf),
+                                sf_token_stride, sf_hidden_stride, _ptr(recv_src_token),
+                                _ptr(recv_weight), _stream(stream))
+    return _check(rc, "ep_dispatch_fp8")
 
 
 def ep_combine_topk_weights(problem, recv_weight, token_slot, combined_topk_weights,

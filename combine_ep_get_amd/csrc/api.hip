@@ -142,9 +142,62 @@ int ep_dispatch(const ep_problem *p, const uint16_t *x, const float *topk_weight
     if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(token_slot, 4) ||
         !aligned(topk_weights, 4) || !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
         return EP_ERR_INVALID_ARG;
-    return hip_rc(epget::launch_dispatch(copy_params(p), x, topk_weights, token_slot, recv_x,
-                                         recv_src_token, recv_weight,
-                                         static_cast<hipStream_t>(stream)));
+    epget::DispatchArgs a = {};
+    a.x = x;
+    a.w = topk_weights;
+    a.slot = token_slot;
+    a.recv = recv_x;
+    a.recv_src = recv_src_token;
+    a.recv_w = recv_weight;
+    return hip_rc(epget::launch_dispatch(copy_params(p), a, static_cast<hipStream_t>(stream)));
+}
+
+int ep_quantize_fp8(const ep_problem *p, const uint16_t *x, uint8_t *x_fp8, float *x_sf,
+                    void *stream) {
+    int rc = check_shape(p);
+    if (rc != EP_OK) return rc;
+    if (p->hidden % 128 != 0) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!x || !x_fp8 || !x_sf) return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(x_fp8, 16) || !aligned(x_sf, 4)) return EP_ERR_INVALID_ARG;
+    return hip_rc(epget::launch_quantize_fp8(p->num_tokens, p->hidden, x, x_fp8, x_sf,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_fp8(const ep_problem *p, const uint8_t *x_fp8, const float *x_sf,
+                    const float *topk_weights, const int32_t *token_slot, uint8_t *recv_x_fp8,
+                    float *recv_sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                    int32_t *recv_src_token, float *recv_weight, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if (p->hidden % 128 != 0 || sf_token_stride < 1 || sf_hidden_stride < 1)
+        return EP_ERR_INVALID_ARG;
+    const int64_t nsf = p->hidden / 128;
+    const int64_t rows = p->rank_stride_rows * p->num_ranks;
+    // the largest scale index must be addressable
+    if ((rows - 1) > (INT64_MAX - (nsf - 1) * sf_hidden_stride) / sf_token_stride)
+        return EP_ERR_INVALID_ARG;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!x_fp8 || !x_sf || !token_slot || !recv_x_fp8 || !recv_sf) return EP_ERR_INVALID_ARG;
+    if (!aligned(x_fp8, 16) || !aligned(recv_x_fp8, 16) || !aligned(x_sf, 4) ||
+        !aligned(recv_sf, 4) || !aligned(token_slot, 4) || !aligned(topk_weights, 4) ||
+        !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
+        return EP_ERR_INVALID_ARG;
+    epget::CopyParams c = copy_params(p);
+    c.nvec = p->hidden / 16;
+    epget::DispatchArgs a = {};
+    a.x = x_fp8;
+    a.w = topk_weights;
+    a.slot = token_slot;
+    a.recv = recv_x_fp8;
+    a.recv_src = recv_src_token;
+    a.recv_w = recv_weight;
+    a.x_sf = x_sf;
+    a.recv_sf = recv_sf;
+    a.sf_ts = sf_token_stride;
+    a.sf_hs = sf_hidden_stride;
+    a.nsf = static_cast<int32_t>(nsf);
+    return hip_rc(epget::launch_dispatch(c, a, static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine(const ep_problem *p, const uint16_t *y, const int32_t *token_slot,

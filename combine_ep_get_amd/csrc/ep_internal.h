@@ -57,9 +57,25 @@ struct LayoutParams {
 
 struct CopyParams {
     int32_t T, H, K;
-    int32_t nvec;      // H / 8 : 16-byte vectors per row
+    int32_t nvec;      // 16-byte vectors per row (H / 8 for bf16, H / 16 for fp8)
     int32_t vpt;       // vectors per thread (<= kMaxVpt)
     int64_t num_rows;  // R * S
+};
+
+// Pointers of one dispatch.  Rows are moved as 16-byte vectors whatever
+// their element type; x_sf / recv_sf are the optional per-row scale factors
+// (nsf per row; element (row, b) of recv_sf at row * sf_ts + b * sf_hs).
+struct DispatchArgs {
+    const void *x;
+    const float *w;
+    const int32_t *slot;
+    void *recv;
+    int32_t *recv_src;
+    float *recv_w;
+    const float *x_sf;
+    float *recv_sf;
+    int64_t sf_ts, sf_hs;
+    int32_t nsf;
 };
 
 constexpr int kCopyThreads = 128;      // dispatch workgroup size
@@ -67,9 +83,9 @@ constexpr int kMaxVpt = 8;            // dispatch vectors per thread
 constexpr int kCombineMaxThreads = 1024;
 
 hipError_t launch_layout(const LayoutParams &p, hipStream_t stream);
-hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *w,
-                           const int32_t *slot, uint16_t *recv_x, int32_t *recv_src,
-                           float *recv_w, hipStream_t stream);
+hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream);
+hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, float *sf,
+                               hipStream_t stream);
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
                           const float *w, uint16_t *out, hipStream_t stream);
 hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, const int32_t *slot,

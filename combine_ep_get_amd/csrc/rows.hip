@@ -28,37 +28,111 @@ __device__ __forceinline__ bool slot_ok(int32_t s, int64_t num_rows) {
 
 // VPT: 16-byte vectors per thread.  Loads are unconditional (the column is
 // clamped into the row) so the compiler issues them back to back; only the
-// stores are predicated.
+// stores are predicated.  Rows are copied as 16-byte vectors whatever their
+// element type (bf16, or e4m3 codes with per-row scale factors).
 template <int VPT>
-__global__ __launch_bounds__(kCopyThreads) void dispatch_kernel(
-    CopyParams c, const uint16_t *__restrict__ x, const float *__restrict__ w,
-    const int32_t *__restrict__ slot, uint16_t *__restrict__ recv_x,
-    int32_t *__restrict__ recv_src, float *__restrict__ recv_w) {
+__global__ __launch_bounds__(kCopyThreads) void dispatch_kernel(CopyParams c, DispatchArgs a) {
     const int t = blockIdx.x;
-    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(t) * c.H);
+    const int32_t *srow = a.slot + static_cast<int64_t>(t) * c.K;
+    const u32x4 *src = static_cast<const u32x4 *>(a.x) + static_cast<int64_t>(t) * c.nvec;
+    u32x4 *recv = static_cast<u32x4 *>(a.recv);
     const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
-    // source index and weight of each received row (written once per token)
-    if (blockIdx.y == 0 && static_cast<int>(threadIdx.x) < c.K) {
-        const int j = threadIdx.x;
-        const int32_t s = srow[j];
-        if (slot_ok(s, c.num_rows)) {
-            if (recv_src) recv_src[s] = t;
-            if (recv_w) recv_w[s] = w ? w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+    if (blockIdx.y == 0) {
+        // source index and weight of each received row (written once per token)
+        if (static_cast<int>(threadIdx.x) < c.K) {
+            const int j = threadIdx.x;
+            const int32_t s = srow[j];
+            if (slot_ok(s, c.num_rows)) {
+                if (a.recv_src) a.recv_src[s] = t;
+                if (a.recv_w) a.recv_w[s] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+            }
+        }
+        // per-row scale factors, one thread per block of channels
+        if (a.x_sf) {
+            for (int b = threadIdx.x; b < a.nsf; b += kCopyThreads) {
+                const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
+                for (int j = 0; j < c.K; ++j) {
+                    const int32_t s = srow[j];
+                    if (slot_ok(s, c.num_rows)) a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
+                }
+            }
         }
     }
     for (int j = 0; j < c.K; ++j) {
         const int32_t s = srow[j];
         if (!slot_ok(s, c.num_rows)) continue;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(recv_x + static_cast<int64_t>(s) * c.H);
+        u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int col = v0 + v * kCopyThreads;
             if (col < c.nvec) dst[col] = buf[v];
         }
+    }
+}
+
+// e4m3 (OCP "fn": bias 7, 3 mantissa bits, largest finite 448, no
+// infinities) code of v: nearest value with ties to even, magnitudes above
+// 448 saturate, NaN gives 0x7F.  Below 2^-6 the grid is the subnormal step
+// 2^-9; above, the mantissa is rounded at 2^(e-3) for v in [2^e, 2^(e+1)).
+// Scaling by powers of two is exact and rintf rounds half to even.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a != a) return 0x7Fu;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | static_cast<uint32_t>(rintf(a * 512.0f));
+    int e = static_cast<int>((u >> 23) & 0xFFu) - 127;
+    int m = static_cast<int>(rintf(ldexpf(a, 3 - e)));  // 8..16
+    if (m == 16) {
+        m = 8;
+        e += 1;
+    }
+    return sign | static_cast<uint32_t>(((e + 7) << 3) | (m - 8));
+}
+
+// Per-token, per-128-channel e4m3 quantisation: 16 lanes hold a block of
+// 128 channels (8 bf16 each), so a wave covers 4 blocks and a workgroup of
+// kQuantThreads covers kQuantThreads / 2 channels of one token.
+constexpr int kQuantThreads = 256;
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(int32_t H, const uint16_t *__restrict__ x,
+                                                                     uint8_t *__restrict__ q,
+                                                                     float *__restrict__ sf) {
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x & 15;
+    const int blk = blockIdx.y * (kQuantThreads / 16) + (threadIdx.x >> 4);
+    const int nb = H / 128;
+    const bool live = blk < nb;
+    const int64_t off = static_cast<int64_t>(t) * H + static_cast<int64_t>(min(blk, nb - 1)) * 128 + lane * 8;
+    const u32x4 in = *reinterpret_cast<const u32x4 *>(x + off);
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f[2 * k] = __uint_as_float(in[k] << 16);
+        f[2 * k + 1] = __uint_as_float(in[k] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[k]));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        lo |= f32_to_e4m3(f[k] * inv) << (8 * k);
+        hi |= f32_to_e4m3(f[4 + k] * inv) << (8 * k);
+    }
+    if (live) {
+        uint2 out;
+        out.x = lo;
+        out.y = hi;
+        *reinterpret_cast<uint2 *>(q + off) = out;
+        if (lane == 0) sf[static_cast<int64_t>(t) * nb + blk] = amax / 448.0f;
     }
 }
 
@@ -165,19 +239,16 @@ void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
     *splits = static_cast<int32_t>((nvec + n - 1) / n);
 }
 
-hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *w,
-                           const int32_t *slot, uint16_t *recv_x, int32_t *recv_src,
-                           float *recv_w, hipStream_t stream) {
+hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream) {
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, &splits, &vpt);
     CopyParams p = c;
     p.vpt = vpt;
     dim3 grid(c.T, splits);
     switch (vpt) {
-#define EP_DISPATCH_CASE(V)                                                                   \
-    case V:                                                                                   \
-        dispatch_kernel<V><<<grid, kCopyThreads, 0, stream>>>(p, x, w, slot, recv_x, recv_src, \
-                                                              recv_w);                        \
+#define EP_DISPATCH_CASE(V)                                                \
+    case V:                                                                \
+        dispatch_kernel<V><<<grid, kCopyThreads, 0, stream>>>(p, a);       \
         break;
         EP_DISPATCH_CASE(1)
         EP_DISPATCH_CASE(2)
@@ -190,6 +261,15 @@ hipError_t launch_dispatch(const CopyParams &c, const uint16_t *x, const float *
 #undef EP_DISPATCH_CASE
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, float *sf,
+                               hipStream_t stream) {
+    const int nb = H / 128;
+    const int per_block = kQuantThreads / 16;
+    dim3 grid(T, (nb + per_block - 1) / per_block);
+    quantize_fp8_kernel<<<grid, kQuantThreads, 0, stream>>>(H, x, q, sf);
     return hipGetLastError();
 }
 

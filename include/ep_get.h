@@ -175,6 +175,42 @@ int ep_combine(const ep_problem *problem, const uint16_t *y,
                const int32_t *token_slot, const float *topk_weights,
                uint16_t *out, void *stream);
 
+/* FP8 (e4m3) quantisation of token rows for FP8 dispatch: one fp32 scale per
+ * token and block of 128 channels, sf = amax / 448, codes = the nearest e4m3
+ * value (OCP "fn": bias 7, 3 mantissa bits, largest 448; ties to even,
+ * larger magnitudes saturate) of x * (448 / amax), all in fp32; an all-zero
+ * block gets sf = 0 and zero codes.  The pages show FP8 dispatch with scale
+ * factors ([SYM] §6.1 sf arguments, §9.2 use_fp8_dispatch) but not the
+ * quantisation rule; this is the reading taken.  Requires H % 128 == 0.
+ *
+ *   x      [T,H] bf16 device, 16-byte aligned
+ *   x_fp8  [T,H] uint8 device (e4m3 codes), 16-byte aligned
+ *   x_sf   [T,H/128] fp32 device, token-major */
+int ep_quantize_fp8(const ep_problem *problem, const uint16_t *x, uint8_t *x_fp8,
+                    float *x_sf, void *stream);
+
+/* FP8 dispatch: as ep_dispatch, with rows of H e4m3 bytes and each row's
+ * H/128 scale factors ([SYM] §6.1: sf, sf_token_stride, sf_hidden_stride).
+ * The scale of received row r and channel block b goes to
+ * recv_sf[r * sf_token_stride + b * sf_hidden_stride]: token-major is
+ * (H/128, 1); the TMA-aligned column-major layout of [V2] (elastic.py block)
+ * is (1, R*S rounded up to the alignment).  recv_sf must hold
+ * (R*S-1)*sf_token_stride + (H/128-1)*sf_hidden_stride + 1 floats.
+ * Requires H % 128 == 0 and strides >= 1.
+ *
+ *   x_fp8        [T,H] uint8 device, 16-byte aligned
+ *   x_sf         [T,H/128] fp32 device, token-major
+ *   topk_weights [T,K] fp32 device, or NULL (every weight is 1)
+ *   token_slot   [T,K] int32 device, from ep_get_layout
+ *   recv_x_fp8   [R*S,H] uint8 device, 16-byte aligned
+ *   recv_sf      fp32 device, see above
+ *   recv_src_token, recv_weight: as in ep_dispatch (may be NULL) */
+int ep_dispatch_fp8(const ep_problem *problem, const uint8_t *x_fp8, const float *x_sf,
+                    const float *topk_weights, const int32_t *token_slot,
+                    uint8_t *recv_x_fp8, float *recv_sf, int64_t sf_token_stride,
+                    int64_t sf_hidden_stride, int32_t *recv_src_token, float *recv_weight,
+                    void *stream);
+
 /* Combined top-k weights: combined_topk_weights[t,j] = recv_weight[token_slot[t,j]]
  * (0 for slots outside [0, R*S)) — the per-row weights that travelled with
  * the dispatched rows, gathered back into token order, as combine returns

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ep
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text))
+    return set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text))
 
 
 def test_header_and_binding_agree():
@@ -88,3 +88,16 @@ def test_bad_pointers_rejected():
     # cumulative counter must be 8-byte aligned
     assert lib.ep_get_layout(ctypes.byref(p), *args, a + 4, a, need, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_read_status(None, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_fp8_argument_checks():
+    lib = ep.load()
+    a = 1 << 20
+    p = P(H=7168 + 8)   # not a multiple of 128
+    assert lib.ep_quantize_fp8(ctypes.byref(p), a, a, a, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_fp8(ctypes.byref(p), a, a, a, a, a, a, 56, 1, a, a, None) == ep.EP_ERR_INVALID_ARG
+    p = P()
+    # non-positive scale strides
+    assert lib.ep_dispatch_fp8(ctypes.byref(p), a, a, a, a, a, a, 0, 1, a, a, None) == ep.EP_ERR_INVALID_ARG
+    # misaligned fp8 rows
+    assert lib.ep_dispatch_fp8(ctypes.byref(p), a + 8, a, a, a, a, a, 56, 1, a, a, None) == ep.EP_ERR_INVALID_ARG

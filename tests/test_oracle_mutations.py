@@ -64,7 +64,8 @@ def _pin_suite():
     fp8pins.test_e4m3_rounding_matches_torch()
     fp8pins.test_quantize_matches_restatement("tiny")
     fp8pins.test_quantize_zero_block_and_extremes()
-    fp8pins.test_dispatch_fp8_moves_codes_and_scales(True)
+    # token-major scales: a planted stride mistake then stays inside the buffer
+    fp8pins.test_dispatch_fp8_moves_codes_and_scales(False)
 
 
 def test_unmutated_build_passes(tmp_path):

@@ -1,0 +1,101 @@
+"""FP8 quantisation and FP8 dispatch: HIP path vs the CPU oracle, bit for
+bit (codes, scales, rows, scale placement in both layouts)."""
+import numpy as np
+import pytest
+import torch
+
+import ep_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ep():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import combine_ep_get_amd as ep
+    ep.load()
+    return ep
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_quantize(ep, x_u16):
+    T, H = x_u16.shape
+    p = ep.Problem.make(T, H, 8, 1, 1, 1, 1, 1)
+    q = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+    ep.ep_quantize_fp8(p, dev(x_u16.view(np.int16)), q, sf)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sf.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode128", "prefill4k", "zipf8k"])
+def test_quantize_parity(ep, name):
+    inp = ep_inputs.make_inputs(name)
+    q, sf = gpu_quantize(ep, inp.x)
+    rq, rsf = oracle.quantize_fp8(inp.x)
+    np.testing.assert_array_equal(sf, rsf)
+    np.testing.assert_array_equal(q, rq)
+
+
+def test_quantize_ties_subnormals_and_zero_blocks(ep):
+    # block 0: amax 448 makes the scale exactly 1, so the values below land
+    # on e4m3 rounding midpoints and in the subnormal range unchanged
+    mags = oracle.e4m3_to_float(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([[448.0], mids[:63], -mids[63:126], [0.001, -0.0005]])[:128]
+    row = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    x = np.zeros((3, 512), np.int16)
+    x[0, :128] = row
+    rng = np.random.default_rng(0)
+    x[1] = ep_inputs.bf16_normal(rng, (512,)).view(np.int16) * 0  # all-zero row
+    x[2] = ep_inputs.bf16_normal(rng, (512,)).view(np.int16)
+    x = x.view(np.uint16)
+    q, sf = gpu_quantize(ep, x)
+    rq, rsf = oracle.quantize_fp8(x)
+    np.testing.assert_array_equal(sf, rsf)
+    np.testing.assert_array_equal(q, rq)
+
+
+@pytest.mark.parametrize("name,column_major", [("tiny", False), ("decode128", True),
+                                               ("prefill4k", False), ("prefill4k", True),
+                                               ("zipf8k", True)])
+def test_dispatch_fp8_parity(ep, name, column_major):
+    inp = ep_inputs.make_inputs(name)
+    wl = inp.wl
+    counts = np.bincount(inp.topk_idx.ravel(), minlength=wl.E)
+    S = int((counts.reshape(wl.R, -1).sum(1)).max())
+    rows = wl.R * S
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, wl.G)
+    q, sf = oracle.quantize_fp8(inp.x)
+    rq, rsf, (ts, hs), rsrc, rw = oracle.dispatch_fp8(q, sf, lay.token_slot, rows, inp.topk_weights,
+                                                     column_major_sf=column_major)
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, 1, S)
+    bufs = ep.alloc_layout(p)
+    ep.ep_get_layout(p, dev(inp.topk_idx), *bufs.args())
+    g_q = torch.empty((rows, wl.H), dtype=torch.uint8, device="cuda")
+    g_sf = torch.full((rsf.size,), float("nan"), dtype=torch.float32, device="cuda")
+    g_src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch_fp8(p, dev(q), dev(sf), dev(inp.topk_weights), bufs.token_slot, g_q, g_sf, ts, hs,
+                       g_src, g_w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), lay.token_slot)
+    s = lay.token_slot.ravel()
+    np.testing.assert_array_equal(g_q.cpu().numpy()[s], rq[s])
+    nb = wl.H // 128
+    got_sf = g_sf.cpu().numpy()
+    idx = (s[:, None] * ts + np.arange(nb)[None, :] * hs).ravel()
+    np.testing.assert_array_equal(got_sf[idx], rsf[idx])
+    np.testing.assert_array_equal(g_src.cpu().numpy()[s], rsrc[s])
+    np.testing.assert_array_equal(g_w.cpu().numpy()[s], rw[s])
+
+
+def test_fp8_rejects_hidden_not_multiple_of_128(ep):
+    p = ep.Problem.make(16, 200, 8, 2, 2, 1, 1, 64)
+    with pytest.raises(ep.EpError):
+        ep.ep_quantize_fp8(p, 1 << 20, 1 << 20, 1 << 20)
