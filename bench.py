@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--workload", default="prefill4k", choices=sorted(ep_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time graph replays (no host launch cost)")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch (e4m3 rows + per-128-channel scales); combine stays bf16")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COPY_CSV", "WRITE_COPY_CSV"),
@@ -268,6 +270,21 @@ def main():
     if status != ep.EP_OK:
         raise RuntimeError(f"layout status {ep.error_string(status)}")
 
+    run_step = step
+    if args.graph:
+        # one step captured once (on a side stream, as capture requires) and
+        # replayed on `stream`
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            stream_saved, stream = stream, side
+            step()
+            stream = stream_saved
+        torch.cuda.synchronize()
+        run_step = graph.replay
+
     # timed region: exactly `steps` steps between two HIP events on the stream
     # the kernels run on (no events inside: each extra event record leaves the
     # GPU idle for a few microseconds)
@@ -277,7 +294,7 @@ def main():
     t_wall0 = time.perf_counter()
     e_start.record(stream)
     for _ in range(args.steps):
-        step()
+        run_step()
     e_end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -317,7 +334,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "R": wl.R,
                    "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
-                   "dispatch": "fp8" if args.fp8 else "bf16"},
+                   "dispatch": "fp8" if args.fp8 else "bf16",
+                   "launch": "hip_graph" if args.graph else "eager"},
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
         "us_per_phase": {k: v * 1e3 for k, v in phase_ms.items()},
