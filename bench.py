@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time graph replays (no host launch cost)")
+    ap.add_argument("--hier", action="store_true",
+                    help="two-level path: group layout, dispatch via the group buffer, per-group partial combine")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch (e4m3 rows + per-128-channel scales); combine stays bf16")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COPY_CSV", "WRITE_COPY_CSV"),
@@ -243,8 +245,22 @@ def main():
         torch.cuda.synchronize()
         quant_us = qe0.elapsed_time(qe1) / 20 * 1e3
 
+    if args.hier:
+        G = max(wl.G, 2)
+        if wl.R % G:
+            raise SystemExit(f"--hier needs R divisible by the group count ({wl.R} % {G})")
+        p.num_groups = G
+        bufs = ep.alloc_layout(p, dev)
+        SG = wl.T
+        gslot = torch.empty((wl.T, G), dtype=torch.int32, device=dev)
+        gbuf = torch.empty((G * SG, wl.H), dtype=torch.int16, device=dev)
+
     def dispatch_call():
-        if args.fp8:
+        if args.hier:
+            ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot, stream=stream)
+            ep.ep_dispatch_hier(p, d_x, d_w, bufs.token_slot, gslot, SG, gbuf, recv, recv_src,
+                                recv_w, stream=stream)
+        elif args.fp8:
             ep.ep_dispatch_fp8(p, d_q, d_sf, d_w, bufs.token_slot, recv_q, recv_sf, nsf, 1,
                                recv_src, recv_w, stream=stream)
         else:
@@ -259,7 +275,10 @@ def main():
         dispatch_call()
         if ev is not None:
             ev[2].record(stream)
-        ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
+        if args.hier:
+            ep.ep_combine_hier(p, recv, bufs.token_slot, d_w, gslot, SG, gbuf, out, stream=stream)
+        else:
+            ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -335,6 +354,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "R": wl.R,
                    "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
                    "dispatch": "fp8" if args.fp8 else "bf16",
+                   "path": "two-level (group buffer)" if args.hier else "flat",
                    "launch": "hip_graph" if args.graph else "eager"},
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
@@ -354,7 +374,7 @@ def main():
             "algorithmic_bytes": nbytes[dominant],
         },
     }
-    if not args.no_cpu_baseline and not args.fp8:
+    if not args.no_cpu_baseline and not args.fp8 and not args.hier:
         result["cpu_baseline"] = cpu_baseline(wl, inp, S)
     print(json.dumps(result), flush=True)
 

@@ -26,7 +26,8 @@ EP_MAX_TOPK = 32
 
 # Every function the C header declares, checked by the test-suite.
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8", "ep_combine_topk_weights",
+           "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8", "ep_get_group_layout",
+           "ep_dispatch_hier", "ep_combine_hier", "ep_combine_topk_weights",
            "ep_read_status", "ep_error_string")
 
 
@@ -86,6 +87,13 @@ def load():
         lib.ep_quantize_fp8.argtypes = [P] + [vp] * 3 + [vp]
         lib.ep_dispatch_fp8.restype = ctypes.c_int
         lib.ep_dispatch_fp8.argtypes = [P] + [vp] * 6 + [ctypes.c_int64, ctypes.c_int64] + [vp] * 2 + [vp]
+        i64 = ctypes.c_int64
+        lib.ep_get_group_layout.restype = ctypes.c_int
+        lib.ep_get_group_layout.argtypes = [P, vp, i64, vp, vp]
+        lib.ep_dispatch_hier.restype = ctypes.c_int
+        lib.ep_dispatch_hier.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
+        lib.ep_combine_hier.restype = ctypes.c_int
+        lib.ep_combine_hier.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp]
         lib.ep_combine_topk_weights.restype = ctypes.c_int
         lib.ep_combine_topk_weights.argtypes = [P] + [vp] * 3 + [vp]
         lib.ep_read_status.restype = ctypes.c_int
@@ -172,6 +180,30 @@ def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, 
                                 sf_token_stride, sf_hidden_stride, _ptr(recv_src_token),
                                 _ptr(recv_weight), _stream(stream))
     return _check(rc, "ep_dispatch_fp8")
+
+
+def ep_get_group_layout(problem, is_token_in_rank, group_stride_rows, group_slot,
+                        stream=None) -> int:
+    rc = load().ep_get_group_layout(ctypes.byref(problem), _ptr(is_token_in_rank),
+                                    group_stride_rows, _ptr(group_slot), _stream(stream))
+    return _check(rc, "ep_get_group_layout")
+
+
+def ep_dispatch_hier(problem, x, topk_weights, token_slot, group_slot, group_stride_rows,
+                     group_buf, recv_x, recv_src_token=None, recv_weight=None, stream=None) -> int:
+    rc = load().ep_dispatch_hier(ctypes.byref(problem), _ptr(x), _ptr(topk_weights),
+                                 _ptr(token_slot), _ptr(group_slot), group_stride_rows,
+                                 _ptr(group_buf), _ptr(recv_x), _ptr(recv_src_token),
+                                 _ptr(recv_weight), _stream(stream))
+    return _check(rc, "ep_dispatch_hier")
+
+
+def ep_combine_hier(problem, y, token_slot, topk_weights, group_slot, group_stride_rows,
+                    group_buf, out, stream=None) -> int:
+    rc = load().ep_combine_hier(ctypes.byref(problem), _ptr(y), _ptr(token_slot),
+                                _ptr(topk_weights), _ptr(group_slot), group_stride_rows,
+                                _ptr(group_buf), _ptr(out), _stream(stream))
+    return _check(rc, "ep_combine_hier")
 
 
 def ep_combine_topk_weights(problem, recv_weight, token_slot, combined_topk_weights,

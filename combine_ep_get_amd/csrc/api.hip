@@ -227,6 +227,100 @@ int ep_combine_topk_weights(const ep_problem *p, const float *recv_weight,
                                                 static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+int check_groups(const ep_problem *p, int64_t SG) {
+    if (SG < 1 || SG * p->num_groups > INT32_MAX) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+epget::HierParams hier_params(const ep_problem *p, int64_t SG) {
+    epget::HierParams h;
+    h.G = p->num_groups;
+    h.ranks_per_group = p->num_ranks / p->num_groups;
+    h.S = static_cast<int32_t>(p->rank_stride_rows);
+    h.SG = static_cast<int32_t>(SG);
+    h.group_rows = SG * p->num_groups;
+    return h;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_get_group_layout(const ep_problem *p, const uint8_t *is_token_in_rank,
+                        int64_t group_stride_rows, int32_t *group_slot, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_groups(p, group_stride_rows)) != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!is_token_in_rank || !group_slot || !aligned(group_slot, 4)) return EP_ERR_INVALID_ARG;
+    return hip_rc(epget::launch_group_layout(p->num_tokens, p->num_ranks,
+                                             hier_params(p, group_stride_rows), is_token_in_rank,
+                                             group_slot, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_hier(const ep_problem *p, const uint16_t *x, const float *topk_weights,
+                     const int32_t *token_slot, const int32_t *group_slot,
+                     int64_t group_stride_rows, uint16_t *group_buf, uint16_t *recv_x,
+                     int32_t *recv_src_token, float *recv_weight, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_groups(p, group_stride_rows)) != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!x || !token_slot || !group_slot || !group_buf || !recv_x) return EP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(group_buf, 16) || !aligned(recv_x, 16) ||
+        !aligned(token_slot, 4) || !aligned(group_slot, 4) || !aligned(topk_weights, 4) ||
+        !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
+        return EP_ERR_INVALID_ARG;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const epget::HierParams h = hier_params(p, group_stride_rows);
+    // stage 1: each token once to every group it reaches
+    epget::CopyParams c1 = copy_params(p);
+    c1.K = h.G;
+    c1.num_rows = h.group_rows;
+    epget::DispatchArgs a1 = {};
+    a1.x = x;
+    a1.slot = group_slot;
+    a1.recv = group_buf;
+    hipError_t err = epget::launch_dispatch(c1, a1, st);
+    if (err != hipSuccess) return EP_ERR_HIP;
+    // stage 2: group rows to the entries' rows
+    epget::DispatchArgs a2 = {};
+    a2.w = topk_weights;
+    a2.slot = token_slot;
+    a2.recv = recv_x;
+    a2.recv_src = recv_src_token;
+    a2.recv_w = recv_weight;
+    return hip_rc(epget::launch_expand(copy_params(p), h, a2, group_slot, group_buf, st));
+}
+
+int ep_combine_hier(const ep_problem *p, const uint16_t *y, const int32_t *token_slot,
+                    const float *topk_weights, const int32_t *group_slot,
+                    int64_t group_stride_rows, uint16_t *group_buf, uint16_t *out, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if ((rc = check_groups(p, group_stride_rows)) != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    if (!y || !token_slot || !group_slot || !group_buf || !out) return EP_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(group_buf, 16) || !aligned(out, 16) ||
+        !aligned(token_slot, 4) || !aligned(group_slot, 4) || !aligned(topk_weights, 4))
+        return EP_ERR_INVALID_ARG;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const epget::HierParams h = hier_params(p, group_stride_rows);
+    // stage 1: per-(token, group) partials, rounded to bf16 in the group rows
+    hipError_t err = epget::launch_combine_partial(copy_params(p), h, y, token_slot, topk_weights,
+                                                   group_slot, group_buf, st);
+    if (err != hipSuccess) return EP_ERR_HIP;
+    // stage 2: sum of the token's group rows (unit weights)
+    epget::CopyParams c2 = copy_params(p);
+    c2.K = h.G;
+    c2.num_rows = h.group_rows;
+    return hip_rc(epget::launch_combine(c2, group_buf, group_slot, nullptr, out, st));
+}
+
 int ep_read_status(const void *workspace, void *stream) {
     if (!workspace || !aligned(workspace, 4)) return EP_ERR_INVALID_ARG;
     int32_t v = 0;

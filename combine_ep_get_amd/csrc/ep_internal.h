@@ -78,6 +78,13 @@ struct DispatchArgs {
     int32_t nsf;
 };
 
+// Two-level (group) path: G groups of ranks_per_group ranks, rank slices of
+// S rows, group slices of SG rows (group_rows = G * SG).
+struct HierParams {
+    int32_t G, ranks_per_group, S, SG;
+    int64_t group_rows;
+};
+
 constexpr int kCopyThreads = 128;      // dispatch workgroup size
 constexpr int kMaxVpt = 8;            // dispatch vectors per thread
 constexpr int kCombineMaxThreads = 1024;
@@ -88,6 +95,13 @@ hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t 
                                hipStream_t stream);
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
                           const float *w, uint16_t *out, hipStream_t stream);
+hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
+                               int32_t *group_slot, hipStream_t stream);
+hipError_t launch_expand(const CopyParams &c, const HierParams &h, const DispatchArgs &a,
+                         const int32_t *group_slot, const uint16_t *group_buf, hipStream_t stream);
+hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, const uint16_t *y,
+                                  const int32_t *slot, const float *w, const int32_t *group_slot,
+                                  uint16_t *group_buf, hipStream_t stream);
 hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, const int32_t *slot,
                                   float *combined_w, hipStream_t stream);
 

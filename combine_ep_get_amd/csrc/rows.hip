@@ -146,27 +146,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// One thread per 16-byte column vector: a workgroup covers a whole row (or a
-// contiguous piece of it for small batches), so each thread makes exactly
-// one pass.  KG: top-k entries gathered per round (all KG loads in flight).
-// An entry with an invalid slot loads row 0 instead (always in bounds) and
-// its contribution is discarded by a select, so no load sits behind a
-// branch.  The gathered rows and the output row are touched once, so loads
-// and stores carry the non-temporal hint (measured: it keeps the dispatch's
-// freshly written rows from being evicted and written back while combine
-// streams through them).
-template <int KG>
-__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
-    CopyParams c, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
-    const float *__restrict__ w, uint16_t *__restrict__ out) {
-    const int t = blockIdx.x;
-    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
-    const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
-    const int col = blockIdx.y * blockDim.x + threadIdx.x;
-    const int colc = min(col, c.nvec - 1);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+// Folds the top-k rows of one token at 16-byte column colc into acc, in
+// ascending j with fp32 FMA, for the entries whose slot is valid and passes
+// keep(slot).  KG entries are gathered per round, all KG loads in flight; an
+// entry that does not count loads row 0 instead (always in bounds) and is
+// discarded by a select, so no load sits behind a branch.  The rows are read
+// once, so the loads carry the non-temporal hint.
+template <int KG, class Keep>
+__device__ __forceinline__ void gather_fold(const CopyParams &c, const uint16_t *__restrict__ y,
+                                            const int32_t *srow, const float *wrow, int colc,
+                                            Keep keep, float acc[8]) {
     for (int j0 = 0; j0 < c.K; j0 += KG) {
         u32x4 in[KG];
         bool ok[KG];
@@ -175,7 +164,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
         for (int jj = 0; jj < KG; ++jj) {
             const int j = min(j0 + jj, c.K - 1);
             const int32_t s = srow[j];
-            ok[jj] = j0 + jj < c.K && slot_ok(s, c.num_rows);
+            ok[jj] = j0 + jj < c.K && slot_ok(s, c.num_rows) && keep(s);
             wj[jj] = wrow ? wrow[j] : 1.0f;
             const int64_t row = ok[jj] ? s : 0;
             in[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + row * c.H) + colc);
@@ -191,11 +180,167 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
             }
         }
     }
-    if (col < c.nvec) {
-        u32x4 o;
+}
+
+__device__ __forceinline__ u32x4 pack_row(const float acc[8]) {
+    u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H) + col);
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    return o;
+}
+
+struct KeepAll {
+    __device__ bool operator()(int32_t) const { return true; }
+};
+
+// One thread per 16-byte column vector: a workgroup covers a whole row (or a
+// contiguous piece of it for small batches), so each thread makes exactly
+// one pass.  The output row is written once, with the non-temporal hint
+// (measured: with the non-temporal loads it keeps the dispatch's freshly
+// written rows from being evicted and written back while combine streams
+// through them).
+template <int KG>
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
+    CopyParams c, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
+    const float *__restrict__ w, uint16_t *__restrict__ out) {
+    const int t = blockIdx.x;
+    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
+    const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
+    const int col = blockIdx.y * blockDim.x + threadIdx.x;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    gather_fold<KG>(c, y, srow, wrow, min(col, c.nvec - 1), KeepAll{}, acc);
+    if (col < c.nvec)
+        __builtin_nontemporal_store(pack_row(acc), reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H) + col);
+}
+
+// Group of a valid entry slot in the two-level path: rank = slot / S,
+// group = rank / (R / G).
+struct GroupOf {
+    int32_t S, ranks_per_group, g;
+    __device__ bool operator()(int32_t s) const { return (s / S) / ranks_per_group == g; }
+};
+
+// Two-level combine, stage 1: for each group the token reaches, the partial
+// sum over the token's entries in that group, rounded to bf16 into the
+// group buffer row group_slot[t,g].
+template <int KG>
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
+    CopyParams c, HierParams h, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
+    const float *__restrict__ w, const int32_t *__restrict__ group_slot,
+    uint16_t *__restrict__ group_buf) {
+    const int t = blockIdx.x;
+    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
+    const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
+    const int col = blockIdx.y * blockDim.x + threadIdx.x;
+    const int colc = min(col, c.nvec - 1);
+    for (int g = 0; g < h.G; ++g) {
+        const int32_t gs = group_slot[static_cast<int64_t>(t) * h.G + g];
+        if (gs < 0 || gs >= h.group_rows) continue;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        gather_fold<KG>(c, y, srow, wrow, colc, GroupOf{h.S, h.ranks_per_group, g}, acc);
+        if (col < c.nvec) reinterpret_cast<u32x4 *>(group_buf + static_cast<int64_t>(gs) * c.H)[col] = pack_row(acc);
+    }
+}
+
+// Two-level dispatch, stage 2: each group row of the token goes to the
+// entries of that group (with the entry's source index and weight).
+template <int VPT>
+__global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, HierParams h,
+                                                              DispatchArgs a,
+                                                              const int32_t *__restrict__ group_slot,
+                                                              const uint16_t *__restrict__ group_buf) {
+    const int t = blockIdx.x;
+    const int32_t *srow = a.slot + static_cast<int64_t>(t) * c.K;
+    u32x4 *recv = static_cast<u32x4 *>(a.recv);
+    const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    if (blockIdx.y == 0 && static_cast<int>(threadIdx.x) < c.K) {
+        const int j = threadIdx.x;
+        const int32_t s = srow[j];
+        if (slot_ok(s, c.num_rows)) {
+            if (a.recv_src) a.recv_src[s] = t;
+            if (a.recv_w) a.recv_w[s] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+        }
+    }
+    for (int g = 0; g < h.G; ++g) {
+        const int32_t gs = group_slot[static_cast<int64_t>(t) * h.G + g];
+        if (gs < 0 || gs >= h.group_rows) continue;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(group_buf) + static_cast<int64_t>(gs) * c.nvec;
+        u32x4 buf[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
+        const GroupOf in_group{h.S, h.ranks_per_group, g};
+        for (int j = 0; j < c.K; ++j) {
+            const int32_t s = srow[j];
+            if (!slot_ok(s, c.num_rows) || !in_group(s)) continue;
+            u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                const int col = v0 + v * kCopyThreads;
+                if (col < c.nvec) dst[col] = buf[v];
+            }
+        }
+    }
+}
+
+// Group slots: a stable compaction, per group, of the tokens with an entry on
+// one of the group's ranks.  One workgroup per group walks the tokens in
+// tiles of kGroupThreads; a thread reads its token's rank bytes, and a
+// workgroup scan (DPP inside waves, wave totals through LDS) gives positions.
+constexpr int kGroupThreads = 1024;
+
+__device__ __forceinline__ int wave_inclusive_sum_rows(int v) {
+    const int lane = __lane_id();
+    const int row_lane = lane & 15;
+    int t = __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += row_lane >= 1 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += row_lane >= 2 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += row_lane >= 4 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += row_lane >= 8 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x142, 0xF, 0xF, false);  // row_bcast:15
+    v += (lane & 31) >= 16 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x143, 0xF, 0xF, false);  // row_bcast:31
+    v += lane >= 32 ? t : 0;
+    return v;
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_layout_kernel(int32_t T, int32_t R, HierParams h,
+                                                                     const uint8_t *__restrict__ map,
+                                                                     int32_t *__restrict__ group_slot) {
+    __shared__ int s_wsum[kGroupThreads / 64];
+    const int g = blockIdx.x;
+    const int lane = __lane_id(), w = threadIdx.x >> 6;
+    const int r0 = g * h.ranks_per_group;
+    int carry = 0;
+    for (int base = 0; base < T; base += kGroupThreads) {
+        const int t = base + threadIdx.x;
+        const int tc = min(t, T - 1);
+        const uint8_t *row = map + static_cast<int64_t>(tc) * R + r0;
+        int in = 0;
+        for (int r = 0; r < h.ranks_per_group; ++r) in |= row[r];
+        in = (t < T && in) ? 1 : 0;
+        const int incl = wave_inclusive_sum_rows(in);
+        if (lane == 63) s_wsum[w] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < kGroupThreads / 64; ++i) {
+            const int v = s_wsum[i];
+            before += i < w ? v : 0;
+            total += v;
+        }
+        if (t < T) {
+            const int pos = carry + before + incl - in;
+            group_slot[static_cast<int64_t>(t) * h.G + g] = (in && pos < h.SG) ? g * h.SG + pos : -1;
+        }
+        carry += total;
+        __syncthreads();
     }
 }
 
@@ -294,6 +439,52 @@ hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, cons
                                   float *combined_w, hipStream_t stream) {
     const int64_t n = static_cast<int64_t>(c.T) * c.K;
     combine_weights_kernel<<<(n + 255) / 256, 256, 0, stream>>>(c, recv_w, slot, combined_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
+                               int32_t *group_slot, hipStream_t stream) {
+    group_layout_kernel<<<h.G, kGroupThreads, 0, stream>>>(T, R, h, map, group_slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_expand(const CopyParams &c, const HierParams &h, const DispatchArgs &a,
+                         const int32_t *group_slot, const uint16_t *group_buf, hipStream_t stream) {
+    int32_t splits, vpt;
+    copy_grid(c.T, c.nvec, &splits, &vpt);
+    CopyParams p = c;
+    p.vpt = vpt;
+    dim3 grid(c.T, splits);
+    switch (vpt) {
+#define EP_EXPAND_CASE(V)                                                                    \
+    case V:                                                                                  \
+        expand_kernel<V><<<grid, kCopyThreads, 0, stream>>>(p, h, a, group_slot, group_buf); \
+        break;
+        EP_EXPAND_CASE(1)
+        EP_EXPAND_CASE(2)
+        EP_EXPAND_CASE(3)
+        EP_EXPAND_CASE(4)
+        EP_EXPAND_CASE(5)
+        EP_EXPAND_CASE(6)
+        EP_EXPAND_CASE(7)
+        EP_EXPAND_CASE(8)
+#undef EP_EXPAND_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, const uint16_t *y,
+                                  const int32_t *slot, const float *w, const int32_t *group_slot,
+                                  uint16_t *group_buf, hipStream_t stream) {
+    int32_t splits, threads;
+    combine_grid(c.T, c.nvec, &splits, &threads);
+    dim3 grid(c.T, splits);
+    if (c.K <= 4) {
+        combine_partial_kernel<4><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
+    } else {
+        combine_partial_kernel<8><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
+    }
     return hipGetLastError();
 }
 

@@ -211,6 +211,39 @@ int ep_dispatch_fp8(const ep_problem *problem, const uint8_t *x_fp8, const float
                     int64_t sf_hidden_stride, int32_t *recv_src_token, float *recv_weight,
                     void *stream);
 
+/* Two-level (hierarchical) path for G > 1 scale-out groups of R/G ranks:
+ * "DeepEP V2 ElasticBuffer 架构深度分析" (hybrid dispatch selected when there
+ * is more than one scale-out rank; logical topology block) and [V1] §3.2
+ * (ranks grouped by eight) show a dispatch that sends each token once to
+ * every group it needs and expands it inside the group.  Here the group
+ * stage goes through a group buffer of G slices of SG rows ([G*SG, H] bf16):
+ * a token's row in group g is group_slot[t,g] = g*SG + (number of earlier
+ * tokens reaching group g), or -1 if it does not reach g (or would sit at or
+ * past SG).  The group of entry (t,j) is (token_slot[t,j] / S) / (R/G).
+ * Requires SG >= 1 and G*SG <= INT32_MAX.
+ *
+ * ep_get_group_layout: group_slot [T,G] int32 from is_token_in_rank [T,R]
+ *   (an output of ep_get_layout).  SG = T never drops a token.
+ * ep_dispatch_hier: x -> group_buf (one row per token and group), then each
+ *   entry's row is copied from its group's row into recv_x; recv_src_token
+ *   and recv_weight as in ep_dispatch.  recv_x ends up identical to
+ *   ep_dispatch's.
+ * ep_combine_hier: per (token, group) the partial sum over the token's
+ *   entries in that group, folded in fp32 with FMA in ascending j and rounded
+ *   to bf16 into the group row (the value that would cross the scale-out
+ *   link); then out[t] = bf16(sum of its group rows), fp32 accumulate.
+ *   group_buf is overwritten. */
+int ep_get_group_layout(const ep_problem *problem, const uint8_t *is_token_in_rank,
+                        int64_t group_stride_rows, int32_t *group_slot, void *stream);
+int ep_dispatch_hier(const ep_problem *problem, const uint16_t *x, const float *topk_weights,
+                     const int32_t *token_slot, const int32_t *group_slot,
+                     int64_t group_stride_rows, uint16_t *group_buf, uint16_t *recv_x,
+                     int32_t *recv_src_token, float *recv_weight, void *stream);
+int ep_combine_hier(const ep_problem *problem, const uint16_t *y, const int32_t *token_slot,
+                    const float *topk_weights, const int32_t *group_slot,
+                    int64_t group_stride_rows, uint16_t *group_buf, uint16_t *out,
+                    void *stream);
+
 /* Combined top-k weights: combined_topk_weights[t,j] = recv_weight[token_slot[t,j]]
  * (0 for slots outside [0, R*S)) — the per-row weights that travelled with
  * the dispatched rows, gathered back into token order, as combine returns

@@ -64,6 +64,12 @@ def open_library(path: str):
     lib.oracle_quantize_fp8.argtypes = [i32, i32, vp, vp, vp]
     lib.oracle_dispatch_fp8.restype = None
     lib.oracle_dispatch_fp8.argtypes = [i32, i32, i32, i64] + [vp] * 6 + [i64, i64, vp, vp]
+    lib.oracle_group_layout.restype = None
+    lib.oracle_group_layout.argtypes = [i32, i32, i32, i64, vp, vp]
+    lib.oracle_dispatch_hier.restype = None
+    lib.oracle_dispatch_hier.argtypes = [i32, i32, i32, i32, i32, i64, i64] + [vp] * 5
+    lib.oracle_combine_hier.restype = None
+    lib.oracle_combine_hier.argtypes = [i32, i32, i32, i32, i32, i64, i64] + [vp] * 6
     lib.oracle_combine_topk_weights.restype = None
     lib.oracle_combine_topk_weights.argtypes = [i32, i32, i64, vp, vp, vp]
     lib.oracle_double_to_bf16.restype = None
@@ -196,6 +202,51 @@ def combine(y: np.ndarray, token_slot: np.ndarray, topk_weights: np.ndarray | No
     w = None if topk_weights is None else _c(topk_weights, np.float32)
     _load().oracle_combine(T, H, K, y.shape[0], _p(y), _p(slot), _p(w), _p(out))
     return out
+
+
+def group_layout(is_token_in_rank: np.ndarray, G: int, SG: int) -> np.ndarray:
+    """Group slots of the hierarchical path: a stable compaction, per group,
+    of the tokens with an entry in the group ([V2] hybrid dispatch; [V1]
+    §3.2 groups of ranks).  ``[T,G]`` int32, -1 where absent or past SG."""
+    m = _c(is_token_in_rank, np.uint8)
+    T, R = m.shape
+    out = np.empty((T, G), np.int32)
+    _load().oracle_group_layout(T, R, G, SG, _p(m), _p(out))
+    return out
+
+
+def dispatch_hier(x, group_slot, token_slot, R, S, SG, recv_x=None):
+    """Two-level dispatch: rows to the group buffer once per group, then
+    from the group rows to every expert row.  Returns (group_buf, recv_x)."""
+    x = _c(x, np.uint16)
+    gsl = _c(group_slot, np.int32)
+    slot = _c(token_slot, np.int32)
+    T, H = x.shape
+    G = gsl.shape[1]
+    K = slot.shape[1]
+    gbuf = np.zeros((G * SG, H), np.uint16)
+    if recv_x is None:
+        recv_x = np.zeros((R * S, H), np.uint16)
+    _load().oracle_dispatch_hier(T, H, K, R, G, S, SG, _p(x), _p(gsl), _p(slot), _p(gbuf),
+                                 _p(recv_x))
+    return gbuf, recv_x
+
+
+def combine_hier(y, token_slot, topk_weights, group_slot, R, S, SG):
+    """Two-level combine: per-(token, group) partials rounded to bf16, then
+    their sum per token.  Returns (group_buf, out)."""
+    y = _c(y, np.uint16)
+    slot = _c(token_slot, np.int32)
+    gsl = _c(group_slot, np.int32)
+    T, K = slot.shape
+    G = gsl.shape[1]
+    H = y.shape[1]
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    gbuf = np.zeros((G * SG, H), np.uint16)
+    out = np.empty((T, H), np.uint16)
+    _load().oracle_combine_hier(T, H, K, R, G, S, SG, _p(y), _p(slot), _p(w), _p(gsl),
+                                _p(gbuf), _p(out))
+    return gbuf, out
 
 
 def combine_topk_weights(recv_weight: np.ndarray, token_slot: np.ndarray) -> np.ndarray:

@@ -174,6 +174,111 @@ void oracle_dispatch(int32_t T, int32_t H, int32_t K, int64_t num_rows,
 }
 
 /*
+ * Hierarchical (two-level) path.  "DeepEP V2 ElasticBuffer 架构深度分析"
+ * (dispatch launch block, hybrid_dispatch_impl; logical topology block) and
+ * [V1] §3.2 show a dispatch that, when ranks form several scale-out groups,
+ * sends each token once to every group it needs and expands it inside the
+ * group.  No kernel body is printed; the reading taken here:
+ *
+ *   group layout: group_slot[t,g] = g*SG + (number of earlier tokens with an
+ *     entry in group g) for a token with an entry in group g, else -1 (also
+ *     -1 past the group capacity SG);
+ *   dispatch: x[t] -> group_buf[group_slot[t,g]], then each entry's row is
+ *     copied from its group's row: recv_x[token_slot[t,j]] =
+ *     group_buf[group_slot[t, group of token_slot[t,j]]];
+ *   combine: per (t,g) a partial sum over the entries in group g, folded in
+ *     fp32 with fused multiply-add in ascending j and rounded to bf16 in
+ *     group_buf (the value that would cross the scale-out link), then
+ *     out[t] = bf16(sum over groups of the partials).
+ *
+ * The partial is rounded to bf16, a quantisation that decides the result, so
+ * it is computed in the kernel's precision (fp32 FMA); the final sum over
+ * groups is in double.
+ */
+void oracle_group_layout(int32_t T, int32_t R, int32_t G, int64_t SG,
+                         const uint8_t *is_token_in_rank, int32_t *group_slot)
+{
+    const int32_t rpg = R / G;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t pos = 0;
+        for (int64_t t = 0; t < T; ++t) {
+            int in = 0;
+            for (int32_t r = g * rpg; r < (g + 1) * rpg; ++r)
+                if (is_token_in_rank[t * R + r]) in = 1;
+            if (!in) { group_slot[t * G + g] = -1; continue; }
+            group_slot[t * G + g] = pos < SG ? (int32_t)(g * SG + pos) : -1;
+            pos += 1;
+        }
+    }
+}
+
+/* group of a valid slot: rank = slot / S, group = rank / (R/G) */
+static int32_t slot_group(int64_t s, int64_t S, int32_t R, int32_t G) { return (int32_t)((s / S) / (R / G)); }
+
+void oracle_dispatch_hier(int32_t T, int32_t H, int32_t K, int32_t R, int32_t G, int64_t S,
+                          int64_t SG, const uint16_t *x, const int32_t *group_slot,
+                          const int32_t *token_slot, uint16_t *group_buf, uint16_t *recv_x)
+{
+    const int64_t num_rows = (int64_t)R * S, group_rows = (int64_t)G * SG;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t g = 0; g < G; ++g) {
+            int64_t gs = group_slot[t * G + g];
+            if (gs >= 0 && gs < group_rows) memcpy(group_buf + gs * H, x + t * H, (size_t)H * 2);
+        }
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < K; ++j) {
+            int64_t s = token_slot[t * K + j];
+            if (s < 0 || s >= num_rows) continue;
+            int64_t gs = group_slot[t * G + slot_group(s, S, R, G)];
+            if (gs < 0 || gs >= group_rows) continue;
+            memcpy(recv_x + s * H, group_buf + gs * H, (size_t)H * 2);
+        }
+}
+
+static float bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint16_t double_to_bf16(double v);
+
+void oracle_combine_hier(int32_t T, int32_t H, int32_t K, int32_t R, int32_t G, int64_t S,
+                         int64_t SG, const uint16_t *y, const int32_t *token_slot,
+                         const float *topk_weights, const int32_t *group_slot,
+                         uint16_t *group_buf, uint16_t *out)
+{
+    const int64_t num_rows = (int64_t)R * S, group_rows = (int64_t)G * SG;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t g = 0; g < G; ++g) {
+            int64_t gs = group_slot[t * G + g];
+            if (gs < 0 || gs >= group_rows) continue;
+            for (int64_t h = 0; h < H; ++h) {
+                float acc = 0.0f;
+                for (int32_t j = 0; j < K; ++j) {
+                    int64_t s = token_slot[t * K + j];
+                    if (s < 0 || s >= num_rows || slot_group(s, S, R, G) != g) continue;
+                    float w = topk_weights ? topk_weights[t * K + j] : 1.0f;
+                    acc = fmaf(w, bf16_to_float(y[s * H + h]), acc);
+                }
+                group_buf[gs * H + h] = double_to_bf16((double)acc);
+            }
+        }
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t g = 0; g < G; ++g) {
+                int64_t gs = group_slot[t * G + g];
+                if (gs < 0 || gs >= group_rows) continue;
+                acc += (double)bf16_to_float(group_buf[gs * H + h]);
+            }
+            out[t * H + h] = double_to_bf16(acc);
+        }
+}
+
+/*
  * Combined top-k weights: the weight carried by each dispatched row, read
  * back into token order ([SYM] §9.2: combine returns combined_topk_weights
  * beside combined_x).  Slots < 0 or >= num_rows give 0.

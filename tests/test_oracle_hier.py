@@ -1,0 +1,99 @@
+"""Pins for the oracle's hierarchical (two-level) path.
+
+- group slots against a numpy restatement (cumulative sum of the per-group
+  token flags) and against the layout's group_token_count;
+- two-level dispatch must leave exactly the rows the flat dispatch leaves;
+- one-hot weights through the two-level combine return x exactly;
+- weighted two-level combine stays within the bound set by rounding each
+  group partial to bf16, against the flat fp64 combine.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ep_inputs
+import oracle
+
+
+def _setup(name, seed=None):
+    inp = ep_inputs.make_inputs(name, seed=seed)
+    wl = inp.wl
+    counts = np.bincount(inp.topk_idx.ravel(), minlength=wl.E)
+    S = int(counts.reshape(wl.R, -1).sum(1).max())
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, wl.G)
+    return inp, wl, S, lay
+
+
+def restated_group_slots(is_token_in_rank, G, SG):
+    T, R = is_token_in_rank.shape
+    rpg = R // G
+    out = np.full((T, G), -1, np.int64)
+    for g in range(G):
+        flags = is_token_in_rank[:, g * rpg:(g + 1) * rpg].any(1)
+        pos = np.cumsum(flags) - 1
+        ok = flags & (pos < SG)
+        out[ok, g] = g * SG + pos[ok]
+    return out
+
+
+@pytest.mark.parametrize("name,G", [("large16k", 2), ("prefill4k", 2), ("prefill4k", 4), ("zipf8k", 8), ("tiny", 1)])
+def test_group_slots(name, G):
+    inp, wl, S, lay = _setup(name)
+    T = wl.T
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, G)
+    gs = oracle.group_layout(lay.is_token_in_rank, G, T)
+    np.testing.assert_array_equal(gs, restated_group_slots(lay.is_token_in_rank, G, T))
+    np.testing.assert_array_equal((gs >= 0).sum(0), lay.group_token_count)
+    # capacity: a smaller group slice drops the later tokens
+    SG = int(lay.group_token_count.min()) - 1
+    gs2 = oracle.group_layout(lay.is_token_in_rank, G, SG)
+    np.testing.assert_array_equal(gs2, restated_group_slots(lay.is_token_in_rank, G, SG))
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill4k"])
+def test_two_level_dispatch_equals_flat(name):
+    inp, wl, S, lay = _setup(name)
+    G = max(wl.G, 2) if wl.R % 2 == 0 else 1
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, G)
+    gs = oracle.group_layout(lay.is_token_in_rank, G, wl.T)
+    gbuf, rx = oracle.dispatch_hier(inp.x, gs, lay.token_slot, wl.R, S, wl.T)
+    flat, _, _ = oracle.dispatch(inp.x, lay.token_slot, wl.R * S)
+    np.testing.assert_array_equal(rx, flat)
+    # every group row holds its token's row
+    t_idx, g_idx = np.nonzero(gs >= 0)
+    np.testing.assert_array_equal(gbuf[gs[t_idx, g_idx]], inp.x[t_idx])
+
+
+def test_two_level_combine_one_hot_returns_x():
+    inp, wl, S, lay = _setup("tiny")
+    G = 2
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, G)
+    gs = oracle.group_layout(lay.is_token_in_rank, G, wl.T)
+    _, rx = oracle.dispatch_hier(inp.x, gs, lay.token_slot, wl.R, S, wl.T)
+    w = np.zeros_like(inp.topk_weights)
+    w[:, 0] = 1.0
+    _, out = oracle.combine_hier(rx, lay.token_slot, w, gs, wl.R, S, wl.T)
+    np.testing.assert_array_equal(oracle.bf16_to_double(out), oracle.bf16_to_double(inp.x))
+
+
+@pytest.mark.parametrize("name,G", [("tiny", 2), ("decode128", 2), ("decode128", 8)])
+def test_two_level_combine_within_partial_rounding_bound(name, G):
+    inp, wl, S, lay = _setup(name)
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, G)
+    gs = oracle.group_layout(lay.is_token_in_rank, G, wl.T)
+    y = ep_inputs.expert_outputs(wl.R * S, wl.H, seed=4)
+    gbuf, out = oracle.combine_hier(y, lay.token_slot, inp.topk_weights, gs, wl.R, S, wl.T)
+    flat = oracle.bf16_to_double(oracle.combine(y, lay.token_slot, inp.topk_weights))
+    got = oracle.bf16_to_double(out)
+    part = np.zeros_like(flat)
+    for g in range(G):
+        ok = gs[:, g] >= 0
+        part[ok] += np.abs(oracle.bf16_to_double(gbuf[gs[ok, g]]))
+    # rounding a value to bf16 moves it by at most half an ulp, 2^-8 of its
+    # magnitude: once per partial, once for each of the two final results
+    # (fp32 folding error is far smaller)
+    bound = 2.0 ** -8 * (part + np.abs(flat) + np.abs(got)) + 1e-30
+    assert np.all(np.abs(got - flat) <= bound)
+    # G = 1 reduces to a single fp32 partial: equal to the flat fp32 fold
+    if G == 1:
+        np.testing.assert_array_equal(out, oracle.combine(y, lay.token_slot, inp.topk_weights))

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_fp8 as fp8pins
+import test_oracle_hier as hierpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
@@ -41,6 +42,9 @@ MUTATIONS = {
     "fp8_scale_constant": ("const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;",
                            "const float inv = amax > 0.0f ? 240.0f / amax : 0.0f;"),
     "fp8_scale_inverted": ("sf[t * nb + b] = amax / 448.0f;", "sf[t * nb + b] = 448.0f / amax;"),
+    "group_slot_off_by_one": ("group_slot[t * G + g] = pos < SG ? (int32_t)(g * SG + pos) : -1;",
+                              "group_slot[t * G + g] = pos < SG ? (int32_t)(g * SG + pos + 1) : -1;"),
+    "slot_group_modulo": ("return (int32_t)((s / S) / (R / G));", "return (int32_t)((s / S) % G);"),
     "fp8_scale_strides_swapped": ("recv_sf[s * sf_token_stride + b * sf_hidden_stride]",
                                   "recv_sf[s * sf_hidden_stride + b * sf_token_stride]"),
 }
@@ -64,6 +68,9 @@ def _pin_suite():
     fp8pins.test_e4m3_rounding_matches_torch()
     fp8pins.test_quantize_matches_restatement("tiny")
     fp8pins.test_quantize_zero_block_and_extremes()
+    hierpins.test_group_slots("prefill4k", 2)
+    hierpins.test_two_level_dispatch_equals_flat("tiny")
+    hierpins.test_two_level_combine_one_hot_returns_x()
     # token-major scales: a planted stride mistake then stays inside the buffer
     fp8pins.test_dispatch_fp8_moves_codes_and_scales(False)
 

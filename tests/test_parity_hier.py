@@ -1,0 +1,98 @@
+"""Two-level (hierarchical) path: HIP vs the CPU oracle.
+
+Group slots, group rows and received rows bit for bit; the per-(token,
+group) partial rows bit for bit (both sides fold in fp32 with FMA and round
+to bf16); the final combine within the usual tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import ep_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def ep():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import combine_ep_get_amd as ep
+    ep.load()
+    return ep
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run(ep, idx, w, x, E, R, G, S, SG, y=None):
+    T, K = idx.shape
+    H = x.shape[1]
+    p = ep.Problem.make(T, H, E, K, R, G, 1, S)
+    bufs = ep.alloc_layout(p)
+    ep.ep_get_layout(p, dev(idx), *bufs.args())
+    ref = oracle.layout(idx, E, R, S, G)
+    gslot = torch.empty((T, G), dtype=torch.int32, device="cuda")
+    ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot)
+    torch.cuda.synchronize()
+    ref_gs = oracle.group_layout(ref.is_token_in_rank, G, SG)
+    np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), ref.token_slot)
+    np.testing.assert_array_equal(gslot.cpu().numpy(), ref_gs)
+    # dispatch
+    gbuf = torch.zeros((G * SG, H), dtype=torch.int16, device="cuda")
+    recv = torch.zeros((R * S, H), dtype=torch.int16, device="cuda")
+    src = torch.full((R * S,), -1, dtype=torch.int32, device="cuda")
+    d_w = dev(w)
+    ep.ep_dispatch_hier(p, dev(x.view(np.int16)), d_w, bufs.token_slot, gslot, SG, gbuf, recv, src, None)
+    torch.cuda.synchronize()
+    ref_gbuf, ref_rx = oracle.dispatch_hier(x, ref_gs, ref.token_slot, R, S, SG)
+    valid_g = ref_gs[ref_gs >= 0]
+    np.testing.assert_array_equal(u16(gbuf)[valid_g], ref_gbuf[valid_g])
+    s = ref.token_slot[ref.token_slot >= 0]
+    np.testing.assert_array_equal(u16(recv)[s], ref_rx[s])
+    t_of = np.repeat(np.arange(T), K).reshape(T, K)[ref.token_slot >= 0]
+    np.testing.assert_array_equal(src.cpu().numpy()[s], t_of)
+    # combine
+    if y is None:
+        y = ep_inputs.permuted_rows(ref_rx, seed=13)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    gbuf.zero_()
+    ep.ep_combine_hier(p, dev(y.view(np.int16)), bufs.token_slot, d_w, gslot, SG, gbuf, out)
+    torch.cuda.synchronize()
+    ref_pbuf, ref_out = oracle.combine_hier(y, ref.token_slot, w, ref_gs, R, S, SG)
+    np.testing.assert_array_equal(u16(gbuf)[valid_g], ref_pbuf[valid_g])
+    g_ = oracle.bf16_to_double(u16(out))
+    r_ = oracle.bf16_to_double(ref_out)
+    assert np.all(np.abs(g_ - r_) <= ATOL + RTOL * np.abs(r_))
+
+
+@pytest.mark.parametrize("name,G", [("large16k", 2), ("prefill4k", 4), ("zipf8k", 8), ("tiny", 2), ("decode128", 2)])
+def test_hier_workloads(ep, name, G):
+    print(f"[parity-hier] {name} G={G}", flush=True)
+    inp = ep_inputs.make_inputs(name)
+    wl = inp.wl
+    counts = np.bincount(inp.topk_idx.ravel(), minlength=wl.E)
+    S = int(counts.reshape(wl.R, -1).sum(1).max())
+    y = ep_inputs.expert_outputs(wl.R * S, wl.H, seed=8) if wl.T * wl.H < 2e6 else None
+    run(ep, inp.topk_idx, inp.topk_weights, inp.x, wl.E, wl.R, G, S, wl.T, y=y)
+
+
+def test_hier_small_group_capacity_and_empty_entries(ep):
+    rng = np.random.default_rng(17)
+    T, K, E, R, G, H = 2500, 6, 96, 12, 3, 136
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    counts = np.bincount(idx[idx >= 0], minlength=E)
+    S = int(counts.reshape(R, -1).sum(1).max())
+    ref = oracle.layout(idx, E, R, S, G)
+    SG = int(ref.group_token_count.min()) - 10   # the later tokens of each group are dropped
+    run(ep, idx, w, x, E, R, G, S, SG)
