@@ -381,19 +381,35 @@ static float e4m3_magnitude(int c)
     return ldexpf((float)(8 + m), e - 10);             /* (1 + m/8) * 2^(e-7) */
 }
 
-/* Nearest e4m3 code by search over the 127 finite magnitudes, ties to the
- * even code; magnitudes above 448 saturate, NaN maps to 0x7F. */
+/* The 127 finite magnitudes, codes 0..0x7E, filled on first use. */
+static float e4m3_table[0x7F];
+static int e4m3_table_ready = 0;
+
+static float e4m3_mag(int c)
+{
+    if (!e4m3_table_ready) {
+        for (int k = 0; k < 0x7F; ++k) e4m3_table[k] = e4m3_magnitude(k);
+        e4m3_table_ready = 1;
+    }
+    return e4m3_table[c];
+}
+
+/* Nearest e4m3 code, ties to the even code; magnitudes above 448 saturate,
+ * NaN maps to 0x7F.  The finite magnitudes increase with the code, so a
+ * binary search finds the two neighbours of |v|. */
 static uint8_t float_to_e4m3(float v)
 {
     if (isnan(v)) return 0x7F;
     uint8_t sign = signbit(v) ? 0x80 : 0;
     float a = fabsf(v);
     if (a >= 448.0f) return sign | 0x7E;
-    int best = 0;
-    for (int c = 1; c < 0x7F; ++c) {
-        float dc = fabsf(e4m3_magnitude(c) - a), db = fabsf(e4m3_magnitude(best) - a);
-        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    int lo = 0, hi = 0x7E;           /* magnitude(lo) <= a < magnitude(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e4m3_mag(mid) <= a) lo = mid; else hi = mid;
     }
+    float dlo = a - e4m3_mag(lo), dhi = e4m3_mag(hi) - a;
+    int best = dlo < dhi ? lo : (dhi < dlo ? hi : ((lo & 1) == 0 ? lo : hi));
     return sign | (uint8_t)best;
 }
 

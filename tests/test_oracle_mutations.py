@@ -38,7 +38,7 @@ MUTATIONS = {
                             "for (int32_t r = g; r < g + ranks_per_group; ++r)"),
     "empty_id_counted_bad": ("if (e == -1) continue;", ""),
     "row_sum_uses_aligned": ("rows += expert_count[e];", "rows += align_up(expert_count[e], A);"),
-    "e4m3_ties_away": ("(dc == db && (c & 1) == 0)", "(dc == db)"),
+    "e4m3_ties_away": ("((lo & 1) == 0 ? lo : hi)", "hi"),
     "fp8_scale_constant": ("const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;",
                            "const float inv = amax > 0.0f ? 240.0f / amax : 0.0f;"),
     "fp8_scale_inverted": ("sf[t * nb + b] = amax / 448.0f;", "sf[t * nb + b] = 448.0f / amax;"),

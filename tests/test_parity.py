@@ -28,6 +28,13 @@ def ep():
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+def assert_same(got, want, what=""):
+    """Bitwise equality; the fast check first, numpy's report on failure."""
+    got, want = np.asarray(got), np.asarray(want)
+    if got.shape != want.shape or not np.array_equal(got, want):
+        np.testing.assert_array_equal(got, want, err_msg=what)
+
+
 
 def bf16_dev(a_u16):
     return dev(a_u16.view(np.int16))
@@ -53,8 +60,8 @@ def assert_layout_matches(ep, bufs, status, ref):
     assert status == code
     for name in ("expert_count", "expert_offset", "rank_row_count", "rank_token_count",
                  "group_token_count", "is_token_in_rank", "token_slot"):
-        np.testing.assert_array_equal(getattr(bufs, name).cpu().numpy(), getattr(ref, name),
-                                      err_msg=name)
+        assert_same(getattr(bufs, name).cpu().numpy(), getattr(ref, name),
+                                      name)
 
 
 def combine_close(got_u16, ref_u16):
@@ -89,10 +96,10 @@ def run_full(ep, idx, w, x, E, R, G, A, S, y=None, check_src=True):
     s = ref.token_slot.ravel()
     s = s[s >= 0]
     got_rx = host_u16(recv)
-    np.testing.assert_array_equal(got_rx[s], ref_rx[s])
+    assert_same(got_rx[s], ref_rx[s])
     if check_src:
-        np.testing.assert_array_equal(src.cpu().numpy()[s], ref_src[s])
-        np.testing.assert_array_equal(rw.cpu().numpy()[s], ref_rw[s])
+        assert_same(src.cpu().numpy()[s], ref_src[s])
+        assert_same(rw.cpu().numpy()[s], ref_rw[s])
     # combine on expert outputs in the receive layout
     if y is None:
         y = ep_inputs.permuted_rows(ref_rx, seed=11)
@@ -284,7 +291,7 @@ def test_cumulative_expert_counts_and_cached_layout(ep):
     ep.ep_get_layout(p, dev(idx2), *bufs.args())
     ep.ep_get_layout(p, dev(inp.topk_idx), *bufs.args())
     want = 2 * ref.expert_count.astype(np.int64) + ref2.expert_count
-    np.testing.assert_array_equal(bufs.cumulative_expert_recv.cpu().numpy(), want)
+    assert_same(bufs.cumulative_expert_recv.cpu().numpy(), want)
     # cached mode: the last layout serves two dispatch/combine rounds
     rows = wl.R * S
     recv = torch.empty((rows, wl.H), dtype=torch.int16, device="cuda")
@@ -297,8 +304,8 @@ def test_cumulative_expert_counts_and_cached_layout(ep):
         ep.ep_combine_topk_weights(p, rw, bufs.token_slot, comb_w)
         torch.cuda.synchronize()
         ref_rx, _, _ = oracle.dispatch(x, ref.token_slot, rows, inp.topk_weights)
-        np.testing.assert_array_equal(host_u16(recv)[s], ref_rx[s])
-        np.testing.assert_array_equal(comb_w.cpu().numpy(), inp.topk_weights)
+        assert_same(host_u16(recv)[s], ref_rx[s])
+        assert_same(comb_w.cpu().numpy(), inp.topk_weights)
 
 
 def test_combined_topk_weights_with_invalid_slots(ep):
@@ -316,7 +323,27 @@ def test_combined_topk_weights_with_invalid_slots(ep):
     out = torch.empty((1500, 4), dtype=torch.float32, device="cuda")
     ep.ep_combine_topk_weights(p, dev(recv_w), bufs.token_slot, out)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(out.cpu().numpy(), oracle.combine_topk_weights(recv_w, ref.token_slot))
+    assert_same(out.cpu().numpy(), oracle.combine_topk_weights(recv_w, ref.token_slot))
+
+
+@pytest.mark.parametrize("T,K,E,R,bad,short", [
+    (21000, 8, 256, 16, True, False),    # 165 chunks: count + scan + assign
+    (21000, 8, 256, 16, False, True),
+    (1024, 8, 2048, 8, True, True),      # 8 chunks, 2048 experts: count + summing assign
+    (3000, 3, 12, 3, False, True),       # K not dividing the chunk
+])
+def test_device_errors_in_every_layout_mode(ep, T, K, E, R, bad, short):
+    rng = np.random.default_rng(T + K + E)
+    idx = _route_uniform(rng, T, E, K)
+    if bad:
+        idx[rng.integers(0, T, 5), rng.integers(0, K, 5)] = E + 3
+        idx[7, 0] = -9
+    counts = np.bincount(idx[(idx >= 0) & (idx < E)].ravel(), minlength=E)
+    S = tight_stride(counts, E, R) - (7 if short else 0)
+    ref = oracle.layout(idx, E, R, S)
+    assert ref.status == (oracle.BAD_EXPERT if bad else oracle.CAPACITY)
+    p, bufs, status = gpu_layout(ep, idx, E, R, S, H=64)
+    assert_layout_matches(ep, bufs, status, ref)
 
 
 def test_repeatable(ep):

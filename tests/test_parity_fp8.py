@@ -22,6 +22,13 @@ def ep():
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+def assert_same(got, want, what=""):
+    """Bitwise equality; the fast check first, numpy's report on failure."""
+    got, want = np.asarray(got), np.asarray(want)
+    if got.shape != want.shape or not np.array_equal(got, want):
+        np.testing.assert_array_equal(got, want, err_msg=what)
+
+
 
 def gpu_quantize(ep, x_u16):
     T, H = x_u16.shape
@@ -38,8 +45,8 @@ def test_quantize_parity(ep, name):
     inp = ep_inputs.make_inputs(name)
     q, sf = gpu_quantize(ep, inp.x)
     rq, rsf = oracle.quantize_fp8(inp.x)
-    np.testing.assert_array_equal(sf, rsf)
-    np.testing.assert_array_equal(q, rq)
+    assert_same(sf, rsf)
+    assert_same(q, rq)
 
 
 def test_quantize_ties_subnormals_and_zero_blocks(ep):
@@ -57,8 +64,8 @@ def test_quantize_ties_subnormals_and_zero_blocks(ep):
     x = x.view(np.uint16)
     q, sf = gpu_quantize(ep, x)
     rq, rsf = oracle.quantize_fp8(x)
-    np.testing.assert_array_equal(sf, rsf)
-    np.testing.assert_array_equal(q, rq)
+    assert_same(sf, rsf)
+    assert_same(q, rq)
 
 
 @pytest.mark.parametrize("name,column_major", [("tiny", False), ("decode128", True),
@@ -84,15 +91,15 @@ def test_dispatch_fp8_parity(ep, name, column_major):
     ep.ep_dispatch_fp8(p, dev(q), dev(sf), dev(inp.topk_weights), bufs.token_slot, g_q, g_sf, ts, hs,
                        g_src, g_w)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), lay.token_slot)
+    assert_same(bufs.token_slot.cpu().numpy(), lay.token_slot)
     s = lay.token_slot.ravel()
-    np.testing.assert_array_equal(g_q.cpu().numpy()[s], rq[s])
+    assert_same(g_q.cpu().numpy()[s], rq[s])
     nb = wl.H // 128
     got_sf = g_sf.cpu().numpy()
     idx = (s[:, None] * ts + np.arange(nb)[None, :] * hs).ravel()
-    np.testing.assert_array_equal(got_sf[idx], rsf[idx])
-    np.testing.assert_array_equal(g_src.cpu().numpy()[s], rsrc[s])
-    np.testing.assert_array_equal(g_w.cpu().numpy()[s], rw[s])
+    assert_same(got_sf[idx], rsf[idx])
+    assert_same(g_src.cpu().numpy()[s], rsrc[s])
+    assert_same(g_w.cpu().numpy()[s], rw[s])
 
 
 def test_fp8_rejects_hidden_not_multiple_of_128(ep):

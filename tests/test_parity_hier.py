@@ -27,6 +27,13 @@ def ep():
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+def assert_same(got, want, what=""):
+    """Bitwise equality; the fast check first, numpy's report on failure."""
+    got, want = np.asarray(got), np.asarray(want)
+    if got.shape != want.shape or not np.array_equal(got, want):
+        np.testing.assert_array_equal(got, want, err_msg=what)
+
+
 
 def u16(t):
     return t.cpu().numpy().view(np.uint16)
@@ -43,8 +50,8 @@ def run(ep, idx, w, x, E, R, G, S, SG, y=None):
     ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot)
     torch.cuda.synchronize()
     ref_gs = oracle.group_layout(ref.is_token_in_rank, G, SG)
-    np.testing.assert_array_equal(bufs.token_slot.cpu().numpy(), ref.token_slot)
-    np.testing.assert_array_equal(gslot.cpu().numpy(), ref_gs)
+    assert_same(bufs.token_slot.cpu().numpy(), ref.token_slot)
+    assert_same(gslot.cpu().numpy(), ref_gs)
     # dispatch
     gbuf = torch.zeros((G * SG, H), dtype=torch.int16, device="cuda")
     recv = torch.zeros((R * S, H), dtype=torch.int16, device="cuda")
@@ -54,11 +61,11 @@ def run(ep, idx, w, x, E, R, G, S, SG, y=None):
     torch.cuda.synchronize()
     ref_gbuf, ref_rx = oracle.dispatch_hier(x, ref_gs, ref.token_slot, R, S, SG)
     valid_g = ref_gs[ref_gs >= 0]
-    np.testing.assert_array_equal(u16(gbuf)[valid_g], ref_gbuf[valid_g])
+    assert_same(u16(gbuf)[valid_g], ref_gbuf[valid_g])
     s = ref.token_slot[ref.token_slot >= 0]
-    np.testing.assert_array_equal(u16(recv)[s], ref_rx[s])
+    assert_same(u16(recv)[s], ref_rx[s])
     t_of = np.repeat(np.arange(T), K).reshape(T, K)[ref.token_slot >= 0]
-    np.testing.assert_array_equal(src.cpu().numpy()[s], t_of)
+    assert_same(src.cpu().numpy()[s], t_of)
     # combine
     if y is None:
         y = ep_inputs.permuted_rows(ref_rx, seed=13)
@@ -67,7 +74,7 @@ def run(ep, idx, w, x, E, R, G, S, SG, y=None):
     ep.ep_combine_hier(p, dev(y.view(np.int16)), bufs.token_slot, d_w, gslot, SG, gbuf, out)
     torch.cuda.synchronize()
     ref_pbuf, ref_out = oracle.combine_hier(y, ref.token_slot, w, ref_gs, R, S, SG)
-    np.testing.assert_array_equal(u16(gbuf)[valid_g], ref_pbuf[valid_g])
+    assert_same(u16(gbuf)[valid_g], ref_pbuf[valid_g])
     g_ = oracle.bf16_to_double(u16(out))
     r_ = oracle.bf16_to_double(ref_out)
     assert np.all(np.abs(g_ - r_) <= ATOL + RTOL * np.abs(r_))
