@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--workload", default="prefill4k", choices=sorted(ep_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each phase after writing a 512 MiB scratch buffer (larger than the "
+                         "256 MB last-level cache), as expert compute between phases would")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time graph replays (no host launch cost)")
     ap.add_argument("--hier", action="store_true",
@@ -331,6 +334,38 @@ def main():
         "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
         "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
     }
+    cold_us = None
+    if args.cold:
+        # per-phase durations with the last-level cache flushed before each
+        # phase by a 512 MiB fill outside the timed event pair
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev = cold_ev[i]
+            scratch.fill_(i & 0xFF)
+            ev[0].record(stream)
+            ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
+            ev[1].record(stream)
+            scratch.fill_((i + 1) & 0xFF)
+            ev[2].record(stream)
+            dispatch_call()
+            ev[3].record(stream)
+            scratch.fill_((i + 2) & 0xFF)
+            ev[4].record(stream)
+            if args.hier:
+                ep.ep_combine_hier(p, recv, bufs.token_slot, d_w, gslot, SG, gbuf, out, stream=stream)
+            else:
+                ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
+            ev[5].record(stream)
+        torch.cuda.synchronize()
+        cold_us = {
+            "layout": float(np.mean([e[0].elapsed_time(e[1]) for e in cold_ev])) * 1e3,
+            "dispatch": float(np.mean([e[2].elapsed_time(e[3]) for e in cold_ev])) * 1e3,
+            "combine": float(np.mean([e[4].elapsed_time(e[5]) for e in cold_ev])) * 1e3,
+        }
+        del scratch
+
     nbytes = algorithmic_bytes(wl, fp8=args.fp8)
     total_bytes = sum(nbytes.values())
     eff_gbps = total_bytes / (ms_step * 1e-3) / 1e9
@@ -360,6 +395,7 @@ def main():
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
         "us_per_phase": {k: v * 1e3 for k, v in phase_ms.items()},
         "us_per_phase_note": "separate pass of the same steps with an event pair around each call",
+        "us_per_phase_cold": cold_us,
         "us_per_step": ms_step * 1e3,
         "us_quantize_fp8": quant_us,
         "wall_s_timed": t_wall,

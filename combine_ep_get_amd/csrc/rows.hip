@@ -26,6 +26,9 @@ __device__ __forceinline__ bool slot_ok(int32_t s, int64_t num_rows) {
     return s >= 0 && s < num_rows;
 }
 
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
 // VPT: 16-byte vectors per thread.  Loads are unconditional (the column is
 // clamped into the row) so the compiler issues them back to back; only the
 // stores are predicated.  Rows are copied as 16-byte vectors whatever their
@@ -94,50 +97,52 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return sign | static_cast<uint32_t>(((e + 7) << 3) | (m - 8));
 }
 
-// Per-token, per-128-channel e4m3 quantisation: 16 lanes hold a block of
-// 128 channels (8 bf16 each), so a wave covers 4 blocks and a workgroup of
-// kQuantThreads covers kQuantThreads / 2 channels of one token.
+// Per-token, per-128-channel e4m3 quantisation: 8 lanes hold a block of 128
+// channels (16 bf16 each: two 16-byte loads, one 16-byte store of codes), so
+// a wave covers 8 blocks and a workgroup of kQuantThreads covers
+// 16 * kQuantThreads channels of one token.
 constexpr int kQuantThreads = 256;
+constexpr int kQuantLanesPerBlock = 8;
 
 __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(int32_t H, const uint16_t *__restrict__ x,
                                                                      uint8_t *__restrict__ q,
                                                                      float *__restrict__ sf) {
     const int t = blockIdx.x;
-    const int lane = threadIdx.x & 15;
-    const int blk = blockIdx.y * (kQuantThreads / 16) + (threadIdx.x >> 4);
+    const int lane = threadIdx.x % kQuantLanesPerBlock;
+    const int blk = blockIdx.y * (kQuantThreads / kQuantLanesPerBlock) + threadIdx.x / kQuantLanesPerBlock;
     const int nb = H / 128;
     const bool live = blk < nb;
-    const int64_t off = static_cast<int64_t>(t) * H + static_cast<int64_t>(min(blk, nb - 1)) * 128 + lane * 8;
-    const u32x4 in = *reinterpret_cast<const u32x4 *>(x + off);
-    float f[8];
+    const int64_t off = static_cast<int64_t>(t) * H + static_cast<int64_t>(min(blk, nb - 1)) * 128 + lane * 16;
+    const u32x4 in0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + off));
+    const u32x4 in1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + off) + 1);
+    float f[16];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        f[2 * k] = __uint_as_float(in[k] << 16);
-        f[2 * k + 1] = __uint_as_float(in[k] & 0xFFFF0000u);
+        f[2 * k] = bf16_lo(in0[k]);
+        f[2 * k + 1] = bf16_hi(in0[k]);
+        f[8 + 2 * k] = bf16_lo(in1[k]);
+        f[8 + 2 * k + 1] = bf16_hi(in1[k]);
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[k]));
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(f[k]));
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 16));
+    for (int d = 1; d < kQuantLanesPerBlock; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kQuantLanesPerBlock));
     const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-    uint32_t lo = 0, hi = 0;
+    u32x4 codes;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        lo |= f32_to_e4m3(f[k] * inv) << (8 * k);
-        hi |= f32_to_e4m3(f[4 + k] * inv) << (8 * k);
+    for (int w = 0; w < 4; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) word |= f32_to_e4m3(f[4 * w + k] * inv) << (8 * k);
+        codes[w] = word;
     }
     if (live) {
-        uint2 out;
-        out.x = lo;
-        out.y = hi;
-        *reinterpret_cast<uint2 *>(q + off) = out;
+        *reinterpret_cast<u32x4 *>(q + off) = codes;
         if (lane == 0) sf[static_cast<int64_t>(t) * nb + blk] = amax / 448.0f;
     }
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = static_cast<__bf16>(lo);
@@ -412,7 +417,7 @@ hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream
 hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, float *sf,
                                hipStream_t stream) {
     const int nb = H / 128;
-    const int per_block = kQuantThreads / 16;
+    const int per_block = kQuantThreads / kQuantLanesPerBlock;
     dim3 grid(T, (nb + per_block - 1) / per_block);
     quantize_fp8_kernel<<<grid, kQuantThreads, 0, stream>>>(H, x, q, sf);
     return hipGetLastError();
