@@ -129,13 +129,36 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(int32_t H, 
 #pragma unroll
     for (int d = 1; d < kQuantLanesPerBlock; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kQuantLanesPerBlock));
     const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        f[k] *= inv;
+        nan |= f[k] != f[k];
+    }
     u32x4 codes;
+    if (!nan) {
+        // gfx950's packed conversion to OCP e4m3 rounds to nearest even; the
+        // clamp gives the saturation at +-448 (a scaled value can exceed 448
+        // by an ulp of fp32)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t word = 0;
+        for (int w = 0; w < 4; ++w) {
+            float c[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) word |= f32_to_e4m3(f[4 * w + k] * inv) << (8 * k);
-        codes[w] = word;
+            for (int k = 0; k < 4; ++k) c[k] = fminf(fmaxf(f[4 * w + k], -448.0f), 448.0f);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], word, true);
+            codes[w] = static_cast<uint32_t>(word);
+        }
+    } else {
+        // a NaN (a NaN input, or inf times a zero scale) takes the explicit
+        // encoder, which maps it to 0x7F
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) word |= f32_to_e4m3(f[4 * w + k]) << (8 * k);
+            codes[w] = word;
+        }
     }
     if (live) {
         *reinterpret_cast<u32x4 *>(q + off) = codes;

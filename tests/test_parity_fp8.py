@@ -68,6 +68,48 @@ def test_quantize_ties_subnormals_and_zero_blocks(ep):
     assert_same(q, rq)
 
 
+def test_quantize_every_bf16_value_at_unit_scale(ep):
+    # every bf16 value with |v| <= 448, 127 to a block behind a leading 448
+    # (which makes the block's scale exactly 1): the conversion is checked on
+    # each input the format can hold
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    vals = vals[keep]
+    nblk = -(-vals.size // 127)
+    body = np.zeros(nblk * 127, np.float32)
+    body[:vals.size] = vals
+    blocks = np.zeros((nblk, 128), np.float32)
+    blocks[:, 0] = 448.0
+    blocks[:, 1:] = body.reshape(nblk, 127)
+    nb_row = 16
+    rows = -(-nblk // nb_row)
+    x = np.zeros((rows * nb_row, 128), np.float32)
+    x[:nblk] = blocks
+    x = x.reshape(rows, nb_row * 128)
+    x_u16 = (x.view(np.uint32) >> 16).astype(np.uint16)
+    q, sf = gpu_quantize(ep, x_u16)
+    rq, rsf = oracle.quantize_fp8(x_u16)
+    assert_same(sf, rsf)
+    assert_same(q, rq)
+
+
+def test_quantize_nan_and_inf_inputs(ep):
+    # not finite inputs: a NaN is skipped by the block maximum and encodes as
+    # 0x7F; an infinity makes the scale infinite and every code of its block
+    # zero except its own, which is NaN times zero
+    rng = np.random.default_rng(5)
+    x = ep_inputs.bf16_normal(rng, (4, 512)).view(np.uint16).copy()
+    x[0, 3] = 0x7FC0          # NaN
+    x[1, 130] = 0x7F80        # +inf
+    x[2, 300] = 0xFF80        # -inf
+    x[3, 511] = 0xFFC1        # NaN with payload and sign
+    q, sf = gpu_quantize(ep, x)
+    rq, rsf = oracle.quantize_fp8(x)
+    assert_same(sf, rsf)
+    assert_same(q, rq)
+
+
 @pytest.mark.parametrize("name,column_major", [("tiny", False), ("decode128", True),
                                                ("prefill4k", False), ("prefill4k", True),
                                                ("zipf8k", True)])
