@@ -1,0 +1,107 @@
+// Device helpers shared by the layout and row kernels of libepget: wave64
+// prefix sums and the 16-byte row copy of dispatch.  Internal header.
+#pragma once
+
+#include "ep_internal.h"
+
+namespace epget {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bool slot_ok(int32_t s, int64_t num_rows) {
+    return s >= 0 && s < num_rows;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave with DPP moves: shifts
+// by 1, 2, 4, 8 inside each row of 16 lanes, then the broadcasts of lane 15
+// and lane 31 into the following rows.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = __lane_id();
+    const int row_lane = lane & 15;
+    int t = __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += row_lane >= 1 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += row_lane >= 2 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += row_lane >= 4 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += row_lane >= 8 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x142, 0xF, 0xF, false);  // row_bcast:15
+    v += (lane & 31) >= 16 ? t : 0;
+    t = __builtin_amdgcn_mov_dpp(v, 0x143, 0xF, 0xF, false);  // row_bcast:31
+    v += lane >= 32 ? t : 0;
+    return v;
+}
+
+// Dispatch of one token by one workgroup of kCopyThreads threads, which owns
+// the 16-byte column vectors v0 + v * kCopyThreads (v < VPT) of the row.
+// Rows are moved as 16-byte vectors whatever their element type (bf16, or
+// e4m3 codes with per-row scale factors).
+//
+// load_token_row: the thread's vectors of x[t].  Loads are unconditional
+// (the column is clamped into the row) so they issue back to back.
+template <int VPT>
+__device__ __forceinline__ void load_token_row(const CopyParams &c, const DispatchArgs &a, int t, int v0,
+                                               u32x4 (&buf)[VPT]) {
+    const u32x4 *src = static_cast<const u32x4 *>(a.x) + static_cast<int64_t>(t) * c.nvec;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
+}
+
+// Slot j of the token, held by lane j of every wave (j < K <= 32): a
+// readlane puts it in a scalar register, so walking the K rows waits on no
+// memory (the slots are loaded once, with the row, before any store).
+__device__ __forceinline__ int32_t slot_of(int32_t lane_slot, int j) {
+    return __builtin_amdgcn_readlane(lane_slot, j);
+}
+
+// From this many vectors per thread on, a workgroup waits for one row's
+// stores to complete before it issues the next row's.
+constexpr int kRowWaitMinVpt = 4;
+
+// s_waitcnt with vmcnt = 0 and the other counters at their maximum (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// store_token_rows: the vectors to the K destination rows (a row outside
+// [0, num_rows) is skipped); with `meta`, also each received row's source
+// token and weight and its scale factors.  lane_slot as for slot_of.
+template <int VPT>
+__device__ __forceinline__ void store_token_rows(const CopyParams &c, const DispatchArgs &a, int t, int v0,
+                                                 bool meta, int32_t lane_slot, const u32x4 (&buf)[VPT]) {
+    if (meta) {
+        if (static_cast<int>(threadIdx.x) < c.K) {
+            const int j = threadIdx.x;  // lane j of wave 0
+            if (slot_ok(lane_slot, c.num_rows)) {
+                if (a.recv_src) a.recv_src[lane_slot] = t;
+                if (a.recv_w) a.recv_w[lane_slot] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+            }
+        }
+        // per-row scale factors, one thread per block of channels
+        if (a.x_sf) {
+            for (int b = threadIdx.x; b < a.nsf; b += kCopyThreads) {
+                const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
+                for (int j = 0; j < c.K; ++j) {
+                    const int32_t s = slot_of(lane_slot, j);
+                    if (slot_ok(s, c.num_rows)) a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
+                }
+            }
+        }
+    }
+    u32x4 *recv = static_cast<u32x4 *>(a.recv);
+    for (int j = 0; j < c.K; ++j) {
+        const int32_t s = slot_of(lane_slot, j);
+        if (!slot_ok(s, c.num_rows)) continue;
+        u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int col = v0 + v * kCopyThreads;
+            if (col < c.nvec) dst[col] = buf[v];
+        }
+        if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+}
+
+}  // namespace
+}  // namespace epget

@@ -35,7 +35,7 @@
 // (indices clamped into range, a buffer load's range check where a predicate
 // is needed), so each step costs about one memory round trip.
 #include "../../include/ep_get.h"
-#include "ep_internal.h"
+#include "device_common.h"
 
 namespace epget {
 namespace {
@@ -72,27 +72,6 @@ struct I32Buffer {
         return __builtin_amdgcn_raw_buffer_load_b32(rsrc, valid ? i * 4u : 0xFFFFFFFCu, 0, 0);
     }
 };
-
-// Inclusive prefix sum across the 64 lanes of a wave with DPP moves: shifts
-// by 1, 2, 4, 8 inside each row of 16 lanes, then the broadcasts of lane 15
-// and lane 31 into the following rows.
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-    const int lane = __lane_id();
-    const int row_lane = lane & 15;
-    int t = __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, false);  // row_shr:1
-    v += row_lane >= 1 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, false);  // row_shr:2
-    v += row_lane >= 2 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    v += row_lane >= 4 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, false);  // row_shr:8
-    v += row_lane >= 8 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x142, 0xF, 0xF, false);  // row_bcast:15
-    v += (lane & 31) >= 16 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x143, 0xF, 0xF, false);  // row_bcast:31
-    v += lane >= 32 ? t : 0;
-    return v;
-}
 
 // Loads the n (<= kChunkEntries) ids at src into s_idx.  Every thread issues
 // its loads back to back (indices clamped into range, so no load sits behind

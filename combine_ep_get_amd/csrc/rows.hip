@@ -15,65 +15,25 @@
 // multiply-add, and rounds once to bf16 (round-to-nearest-even, the
 // hardware's packed bf16 conversion).
 #include "../../include/ep_get.h"
-#include "ep_internal.h"
+#include "device_common.h"
 
 namespace epget {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bool slot_ok(int32_t s, int64_t num_rows) {
-    return s >= 0 && s < num_rows;
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// VPT: 16-byte vectors per thread.  Loads are unconditional (the column is
-// clamped into the row) so the compiler issues them back to back; only the
-// stores are predicated.  Rows are copied as 16-byte vectors whatever their
-// element type (bf16, or e4m3 codes with per-row scale factors).
+// One workgroup per (token, run of columns): each thread loads its VPT
+// vectors of x[t] once and stores them to all K destination rows; the
+// workgroup with blockIdx.y == 0 also writes the rows' metadata.
 template <int VPT>
 __global__ __launch_bounds__(kCopyThreads) void dispatch_kernel(CopyParams c, DispatchArgs a) {
     const int t = blockIdx.x;
-    const int32_t *srow = a.slot + static_cast<int64_t>(t) * c.K;
-    const u32x4 *src = static_cast<const u32x4 *>(a.x) + static_cast<int64_t>(t) * c.nvec;
-    u32x4 *recv = static_cast<u32x4 *>(a.recv);
     const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    const int32_t lane_slot = a.slot[static_cast<int64_t>(t) * c.K + min(static_cast<int>(__lane_id()), c.K - 1)];
     u32x4 buf[VPT];
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
-    if (blockIdx.y == 0) {
-        // source index and weight of each received row (written once per token)
-        if (static_cast<int>(threadIdx.x) < c.K) {
-            const int j = threadIdx.x;
-            const int32_t s = srow[j];
-            if (slot_ok(s, c.num_rows)) {
-                if (a.recv_src) a.recv_src[s] = t;
-                if (a.recv_w) a.recv_w[s] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
-            }
-        }
-        // per-row scale factors, one thread per block of channels
-        if (a.x_sf) {
-            for (int b = threadIdx.x; b < a.nsf; b += kCopyThreads) {
-                const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
-                for (int j = 0; j < c.K; ++j) {
-                    const int32_t s = srow[j];
-                    if (slot_ok(s, c.num_rows)) a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
-                }
-            }
-        }
-    }
-    for (int j = 0; j < c.K; ++j) {
-        const int32_t s = srow[j];
-        if (!slot_ok(s, c.num_rows)) continue;
-        u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const int col = v0 + v * kCopyThreads;
-            if (col < c.nvec) dst[col] = buf[v];
-        }
-    }
+    load_token_row<VPT>(c, a, t, v0, buf);
+    store_token_rows<VPT>(c, a, t, v0, blockIdx.y == 0, lane_slot, buf);
 }
 
 // e4m3 (OCP "fn": bias 7, 3 mantissa bits, largest finite 448, no
@@ -282,15 +242,14 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, Hier
                                                               const int32_t *__restrict__ group_slot,
                                                               const uint16_t *__restrict__ group_buf) {
     const int t = blockIdx.x;
-    const int32_t *srow = a.slot + static_cast<int64_t>(t) * c.K;
     u32x4 *recv = static_cast<u32x4 *>(a.recv);
     const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    const int32_t lane_slot = a.slot[static_cast<int64_t>(t) * c.K + min(static_cast<int>(__lane_id()), c.K - 1)];
     if (blockIdx.y == 0 && static_cast<int>(threadIdx.x) < c.K) {
-        const int j = threadIdx.x;
-        const int32_t s = srow[j];
-        if (slot_ok(s, c.num_rows)) {
-            if (a.recv_src) a.recv_src[s] = t;
-            if (a.recv_w) a.recv_w[s] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+        const int j = threadIdx.x;  // lane j of wave 0
+        if (slot_ok(lane_slot, c.num_rows)) {
+            if (a.recv_src) a.recv_src[lane_slot] = t;
+            if (a.recv_w) a.recv_w[lane_slot] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
         }
     }
     for (int g = 0; g < h.G; ++g) {
@@ -302,7 +261,7 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, Hier
         for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
         const GroupOf in_group{h.S, h.ranks_per_group, g};
         for (int j = 0; j < c.K; ++j) {
-            const int32_t s = srow[j];
+            const int32_t s = slot_of(lane_slot, j);
             if (!slot_ok(s, c.num_rows) || !in_group(s)) continue;
             u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
 #pragma unroll
@@ -320,24 +279,6 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, Hier
 // workgroup scan (DPP inside waves, wave totals through LDS) gives positions.
 constexpr int kGroupThreads = 1024;
 
-__device__ __forceinline__ int wave_inclusive_sum_rows(int v) {
-    const int lane = __lane_id();
-    const int row_lane = lane & 15;
-    int t = __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, false);  // row_shr:1
-    v += row_lane >= 1 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, false);  // row_shr:2
-    v += row_lane >= 2 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    v += row_lane >= 4 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, false);  // row_shr:8
-    v += row_lane >= 8 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x142, 0xF, 0xF, false);  // row_bcast:15
-    v += (lane & 31) >= 16 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x143, 0xF, 0xF, false);  // row_bcast:31
-    v += lane >= 32 ? t : 0;
-    return v;
-}
-
 __global__ __launch_bounds__(kGroupThreads) void group_layout_kernel(int32_t T, int32_t R, HierParams h,
                                                                      const uint8_t *__restrict__ map,
                                                                      int32_t *__restrict__ group_slot) {
@@ -353,7 +294,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_layout_kernel(int32_t T, 
         int in = 0;
         for (int r = 0; r < h.ranks_per_group; ++r) in |= row[r];
         in = (t < T && in) ? 1 : 0;
-        const int incl = wave_inclusive_sum_rows(in);
+        const int incl = wave_inclusive_sum(in);
         if (lane == 63) s_wsum[w] = incl;
         __syncthreads();
         int before = 0, total = 0;
