@@ -214,11 +214,15 @@ def main():
                     help="capture one step in a HIP graph and time graph replays (no host launch cost)")
     ap.add_argument("--hier", action="store_true",
                     help="two-level path: group layout, dispatch via the group buffer, per-group partial combine")
+    ap.add_argument("--fused", action="store_true",
+                    help="layout and dispatch through ep_layout_dispatch (one kernel for decode-sized batches)")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch (e4m3 rows + per-128-channel scales); combine stays bf16")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="build profiles/traffic.json from rocprofv3 --pmc counter CSVs (no GPU needed)")
     args = ap.parse_args()
+    if args.fused and (args.fp8 or args.hier):
+        ap.error("--fused applies to the flat bf16 path only")
 
     # counter records are kept per workload and mode
     traffic_key = args.workload + ("+fp8" if args.fp8 else "") + ("+two-level" if args.hier else "")
@@ -290,7 +294,7 @@ def main():
         gslot = torch.empty((wl.T, G), dtype=torch.int32, device=dev)
         gbuf = torch.empty((G * SG, wl.H), dtype=torch.int16, device=dev)
 
-    def dispatch_call():
+    def plain_dispatch_call():
         if args.hier:
             ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot, stream=stream)
             ep.ep_dispatch_hier(p, d_x, d_w, bufs.token_slot, gslot, SG, gbuf, recv, recv_src,
@@ -301,10 +305,21 @@ def main():
         else:
             ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, recv_src, recv_w, stream=stream)
 
+    def layout_call():
+        if not args.fused:
+            ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
+
+    def dispatch_call():  # with --fused, layout and dispatch in one call
+        if args.fused:
+            ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv, recv_src, recv_w,
+                                  stream=stream)
+        else:
+            plain_dispatch_call()
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
+        layout_call()
         if ev is not None:
             ev[1].record(stream)
         dispatch_call()
@@ -377,7 +392,7 @@ def main():
             ev = cold_ev[i]
             scratch.fill_(i & 0xFF)
             ev[0].record(stream)
-            ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
+            layout_call()
             ev[1].record(stream)
             scratch.fill_((i + 1) & 0xFF)
             ev[2].record(stream)
@@ -404,7 +419,15 @@ def main():
     nbytes = algorithmic_bytes(wl, fp8=args.fp8)
     total_bytes = sum(nbytes.values())
     eff_gbps = total_bytes / (ms_step * 1e-3) / 1e9
-    dominant = max(("dispatch", "combine"), key=lambda k: phase_ms[k])
+    if args.fused:
+        # layout and dispatch are one launch: report them as one phase
+        fused_ms = phase_ms.pop("layout") + phase_ms.pop("dispatch")
+        phase_ms = {"layout_dispatch": fused_ms, **phase_ms}
+        nbytes = {"layout_dispatch": nbytes["layout"] + nbytes["dispatch"], "combine": nbytes["combine"]}
+        if cold_us is not None:
+            cold_us = {"layout_dispatch": cold_us.pop("layout") + cold_us.pop("dispatch"), **cold_us}
+    dominant = max((k for k in ("dispatch", "layout_dispatch", "combine") if k in phase_ms),
+                   key=lambda k: phase_ms[k])
     achieved = nbytes[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
     # the FP8 mode runs the very same combine launch as the bf16 mode (bf16
     # expert outputs), so the bf16 counter record applies to it
@@ -428,6 +451,7 @@ def main():
                    "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
                    "dispatch": "fp8" if args.fp8 else "bf16",
                    "path": "two-level (group buffer)" if args.hier else "flat",
+                   "layout_dispatch": "one call (ep_layout_dispatch)" if args.fused else "two calls",
                    "launch": "hip_graph" if args.graph else "eager"},
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,

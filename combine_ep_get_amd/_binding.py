@@ -26,7 +26,7 @@ EP_MAX_TOPK = 32
 
 # Every function the C header declares, checked by the test-suite.
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
-           "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8", "ep_get_group_layout",
+           "ep_layout_dispatch", "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8", "ep_get_group_layout",
            "ep_dispatch_hier", "ep_combine_hier", "ep_combine_topk_weights",
            "ep_read_status", "ep_error_string")
 
@@ -81,6 +81,8 @@ def load():
         lib.ep_get_layout.argtypes = [P] + [vp] * 10 + [sz, vp]
         lib.ep_dispatch.restype = ctypes.c_int
         lib.ep_dispatch.argtypes = [P] + [vp] * 6 + [vp]
+        lib.ep_layout_dispatch.restype = ctypes.c_int
+        lib.ep_layout_dispatch.argtypes = [P] + [vp] * 10 + [sz] + [vp] * 5 + [vp]
         lib.ep_combine.restype = ctypes.c_int
         lib.ep_combine.argtypes = [P] + [vp] * 4 + [vp]
         lib.ep_quantize_fp8.restype = ctypes.c_int
@@ -158,6 +160,22 @@ def ep_dispatch(problem, x, topk_weights, token_slot, recv_x, recv_src_token=Non
     rc = load().ep_dispatch(ctypes.byref(problem), _ptr(x), _ptr(topk_weights), _ptr(token_slot),
                             _ptr(recv_x), _ptr(recv_src_token), _ptr(recv_weight), _stream(stream))
     return _check(rc, "ep_dispatch")
+
+
+def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                       rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                       cumulative_expert_recv, workspace, workspace_bytes, x, topk_weights, recv_x,
+                       recv_src_token=None, recv_weight=None, stream=None) -> int:
+    """ep_get_layout followed by ep_dispatch (one kernel for decode-sized batches)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = load().ep_layout_dispatch(ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
+                                   _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
+                                   _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
+                                   _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
+                                   _ptr(x), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_src_token),
+                                   _ptr(recv_weight), _stream(stream))
+    return _check(rc, "ep_layout_dispatch")
 
 
 def ep_combine(problem, y, token_slot, topk_weights, out, stream=None) -> int:

@@ -57,30 +57,12 @@ epget::CopyParams copy_params(const ep_problem *p) {
     return c;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ep_workspace_bytes(const ep_problem *p) {
-    if (check_shape(p) != EP_OK) return 0;
-    const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts,
-                                        p->num_ranks, p->num_groups);
-    return static_cast<size_t>(w.bytes);
-}
-
-int64_t ep_rank_stride_hint(const ep_problem *p) {
-    if (check_shape(p) != EP_OK) return -1;
-    const int64_t L = p->num_experts / p->num_ranks;
-    const int64_t per_token = p->num_topk < L ? p->num_topk : L;
-    const int64_t s = p->num_tokens * per_token + L * (p->expert_alignment - 1);
-    return s > 0 ? s : 1;
-}
-
-int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
+// Validates the layout call's arguments and fills lp.
+int layout_params(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
                   int32_t *expert_offset, int32_t *rank_row_count, int32_t *rank_token_count,
                   int32_t *group_token_count, uint8_t *is_token_in_rank, int32_t *token_slot,
                   int64_t *cumulative_expert_recv, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+                  epget::LayoutParams *out) {
     int rc = check_problem(p);
     if (rc != EP_OK) return rc;
     const bool has_tokens = p->num_tokens > 0;
@@ -96,7 +78,7 @@ int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
                                         p->num_ranks, p->num_groups);
     if (workspace_bytes < static_cast<size_t>(w.bytes)) return EP_ERR_INVALID_ARG;
 
-    epget::LayoutParams lp;
+    epget::LayoutParams &lp = *out;
     lp.topk_idx = topk_idx;
     lp.T = p->num_tokens;
     lp.K = p->num_topk;
@@ -129,15 +111,13 @@ int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
     lp.status = reinterpret_cast<int32_t *>(ws);
     lp.totals = reinterpret_cast<int32_t *>(ws + w.totals_off);
     lp.table = reinterpret_cast<int32_t *>(ws + w.table_off);
-    return hip_rc(epget::launch_layout(lp, static_cast<hipStream_t>(stream)));
+    return EP_OK;
 }
 
-int ep_dispatch(const ep_problem *p, const uint16_t *x, const float *topk_weights,
-                const int32_t *token_slot, uint16_t *recv_x, int32_t *recv_src_token,
-                float *recv_weight, void *stream) {
-    int rc = check_problem(p);
-    if (rc != EP_OK) return rc;
-    if (p->num_tokens == 0) return EP_OK;
+// Validates the bf16 dispatch call's pointers and fills a.
+int dispatch_args(const uint16_t *x, const float *topk_weights, const int32_t *token_slot,
+                  uint16_t *recv_x, int32_t *recv_src_token, float *recv_weight,
+                  epget::DispatchArgs *out) {
     if (!x || !token_slot || !recv_x) return EP_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(token_slot, 4) ||
         !aligned(topk_weights, 4) || !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
@@ -149,7 +129,71 @@ int ep_dispatch(const ep_problem *p, const uint16_t *x, const float *topk_weight
     a.recv = recv_x;
     a.recv_src = recv_src_token;
     a.recv_w = recv_weight;
+    *out = a;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_workspace_bytes(const ep_problem *p) {
+    if (check_shape(p) != EP_OK) return 0;
+    const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts,
+                                        p->num_ranks, p->num_groups);
+    return static_cast<size_t>(w.bytes);
+}
+
+int64_t ep_rank_stride_hint(const ep_problem *p) {
+    if (check_shape(p) != EP_OK) return -1;
+    const int64_t L = p->num_experts / p->num_ranks;
+    const int64_t per_token = p->num_topk < L ? p->num_topk : L;
+    const int64_t s = p->num_tokens * per_token + L * (p->expert_alignment - 1);
+    return s > 0 ? s : 1;
+}
+
+int ep_get_layout(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
+                  int32_t *expert_offset, int32_t *rank_row_count, int32_t *rank_token_count,
+                  int32_t *group_token_count, uint8_t *is_token_in_rank, int32_t *token_slot,
+                  int64_t *cumulative_expert_recv, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    epget::LayoutParams lp;
+    const int rc = layout_params(p, topk_idx, expert_count, expert_offset, rank_row_count,
+                                 rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                                 cumulative_expert_recv, workspace, workspace_bytes, &lp);
+    if (rc != EP_OK) return rc;
+    return hip_rc(epget::launch_layout(lp, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch(const ep_problem *p, const uint16_t *x, const float *topk_weights,
+                const int32_t *token_slot, uint16_t *recv_x, int32_t *recv_src_token,
+                float *recv_weight, void *stream) {
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_tokens == 0) return EP_OK;
+    epget::DispatchArgs a;
+    rc = dispatch_args(x, topk_weights, token_slot, recv_x, recv_src_token, recv_weight, &a);
+    if (rc != EP_OK) return rc;
     return hip_rc(epget::launch_dispatch(copy_params(p), a, static_cast<hipStream_t>(stream)));
+}
+
+int ep_layout_dispatch(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
+                       int32_t *expert_offset, int32_t *rank_row_count, int32_t *rank_token_count,
+                       int32_t *group_token_count, uint8_t *is_token_in_rank, int32_t *token_slot,
+                       int64_t *cumulative_expert_recv, void *workspace, size_t workspace_bytes,
+                       const uint16_t *x, const float *topk_weights, uint16_t *recv_x,
+                       int32_t *recv_src_token, float *recv_weight, void *stream) {
+    epget::LayoutParams lp;
+    int rc = layout_params(p, topk_idx, expert_count, expert_offset, rank_row_count, rank_token_count,
+                           group_token_count, is_token_in_rank, token_slot, cumulative_expert_recv,
+                           workspace, workspace_bytes, &lp);
+    if (rc != EP_OK) return rc;
+    epget::DispatchArgs a = {};
+    if (p->num_tokens > 0) {
+        rc = dispatch_args(x, topk_weights, token_slot, recv_x, recv_src_token, recv_weight, &a);
+        if (rc != EP_OK) return rc;
+    }
+    return hip_rc(epget::launch_layout_dispatch(lp, copy_params(p), a, static_cast<hipStream_t>(stream)));
 }
 
 int ep_quantize_fp8(const ep_problem *p, const uint16_t *x, uint8_t *x_fp8, float *x_sf,

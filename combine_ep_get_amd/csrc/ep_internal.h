@@ -91,6 +91,10 @@ constexpr int kCombineMaxThreads = 1024;
 
 hipError_t launch_layout(const LayoutParams &p, hipStream_t stream);
 hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream);
+// launch_layout then launch_dispatch, as one kernel when the batch is one
+// layout chunk.
+hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, const DispatchArgs &a,
+                                  hipStream_t stream);
 hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, float *sf,
                                hipStream_t stream);
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,

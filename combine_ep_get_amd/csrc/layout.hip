@@ -389,18 +389,26 @@ enum AssignMode {
     kScannedTable = 2  // reads the bases and totals pass 2 wrote
 };
 
-// Slot assignment for one chunk by W waves.  Workgroup 0 writes
-// expert_offset, rank_row_count and the status word (and, unless pass 2 ran,
-// the per-expert / per-rank / per-group counts).
+// Experts each thread of a W-wave assign workgroup scans.
+template <int W>
+constexpr int assign_experts_per_thread() {
+    return ((W >= 16 ? 512 : (W >= 8 ? 1024 : EP_MAX_EXPERTS)) + 64 * W - 1) / (64 * W);
+}
+
+// Slot assignment for chunk c by a workgroup of W waves.  Workgroup 0
+// writes expert_offset, rank_row_count and the status word (and, unless
+// pass 2 ran, the per-expert / per-rank / per-group counts).  Without kWalk
+// everything but the slots is computed (a fused dispatch derives those per
+// token instead).
 //
 // LDS: s_idx [kChunkEntries] | fused: s_hist [pitch], whose expert columns
-// later hold the raw scan; otherwise s_raw [E+1] | s_aln [E+1] | s_wave [W*E].
-template <int W, int kMode>
-__global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
+// later hold the raw scan; otherwise s_raw [E+1] | s_aln [E+1] | s_wave [W*E]
+// (s_wave only with kWalk).
+template <int W, int kMode, bool kWalk>
+__device__ void assign_chunk(const LayoutParams &p, int c) {
     constexpr bool kFused = kMode == kFusedChunk;
     constexpr int NT = 64 * W;
-    constexpr int kMaxExperts = W >= 16 ? 512 : (W >= 8 ? 1024 : EP_MAX_EXPERTS);
-    constexpr int kEPT = (kMaxExperts + NT - 1) / NT;  // experts per thread
+    constexpr int kEPT = assign_experts_per_thread<W>();
     extern __shared__ __align__(16) int smem[];
     __shared__ int s_over;
     __shared__ int s_wsum[2 * W];
@@ -410,7 +418,6 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
     int *s_aln = s_raw + (kFused ? p.pitch : p.E + 1);
     int *s_wave = s_aln + (p.E + 1);
     const int tid = threadIdx.x, w = tid >> 6;
-    const int c = blockIdx.x;
     const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
     const int n = (t1 - t0) * p.K;
     const int64_t first = static_cast<int64_t>(t0) * p.K;
@@ -494,7 +501,8 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
         for (int k = 0; k < kEPT; ++k) base[k] = 0;
         for (int i = tid; i < p.ncols; i += NT) s_hist[i] = 0;
     }
-    for (int i = tid; i < W * p.E; i += NT) s_wave[i] = 0;
+    if (kWalk)
+        for (int i = tid; i < W * p.E; i += NT) s_wave[i] = 0;
     if (kMode != kSumTable && tid == 0) s_over = 0;
     __syncthreads();
     if (kMode == kSumTable) {
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
     }
 
     // 2. per-wave expert counts (and, fused, the whole histogram)
-    entry_pass<NT>(p, n, W, s_idx, kFused ? s_hist : nullptr, s_wave);
+    entry_pass<NT>(p, n, W, s_idx, kFused ? s_hist : nullptr, kWalk ? s_wave : nullptr);
     __syncthreads();
     if (kFused) {
         token_pass<NT>(p, t0, t1, s_idx, s_hist);
@@ -532,14 +540,16 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
         const int e = tid + k * NT;
         if (e < p.E) {
             const int off = s_aln[e] - s_aln[p.div_L(e) * p.L];
-            int h[W];
+            if (kWalk) {
+                int h[W];
 #pragma unroll
-            for (int ww = 0; ww < W; ++ww) h[ww] = s_wave[ww * p.E + e];
-            int b = off + base[k];
+                for (int ww = 0; ww < W; ++ww) h[ww] = s_wave[ww * p.E + e];
+                int b = off + base[k];
 #pragma unroll
-            for (int ww = 0; ww < W; ++ww) {
-                s_wave[ww * p.E + e] = b;
-                b += h[ww];
+                for (int ww = 0; ww < W; ++ww) {
+                    s_wave[ww * p.E + e] = b;
+                    b += h[ww];
+                }
             }
             if (c == 0) p.expert_offset[e] = off;
         }
@@ -549,8 +559,15 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
     if (c == 0 && tid == 0) *p.status = status_code(bad > 0, s_over);
 
     // 4. each wave walks its share of the chunk
-    const int span = wave_span(n, W);
-    wave_assign_slots(p, first, min(n, w * span), min(n, (w + 1) * span), s_wave + w * p.E, s_idx);
+    if (kWalk) {
+        const int span = wave_span(n, W);
+        wave_assign_slots(p, first, min(n, w * span), min(n, (w + 1) * span), s_wave + w * p.E, s_idx);
+    }
+}
+
+template <int W, int kMode>
+__global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
+    assign_chunk<W, kMode, true>(p, blockIdx.x);
 }
 
 // Largest table sum (rows x experts per thread) the assign kernel does itself
@@ -560,7 +577,7 @@ constexpr int kMaxTableSum = 64;
 template <int W>
 hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
     const size_t tail = sizeof(int) * ((p.E + 1) + static_cast<size_t>(W) * p.E);
-    constexpr int kEPT = ((W >= 16 ? 512 : (W >= 8 ? 1024 : EP_MAX_EXPERTS)) + 64 * W - 1) / (64 * W);
+    constexpr int kEPT = assign_experts_per_thread<W>();
     if (p.nchunks == 1) {
         const size_t lds = sizeof(int) * (kChunkEntries + p.pitch) + tail;
         layout_assign_kernel<W, kFusedChunk><<<1, 64 * W, lds, stream>>>(p);
@@ -580,6 +597,81 @@ hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
     if (err != hipSuccess) return err;
     layout_assign_kernel<W, kScannedTable><<<p.nchunks, 64 * W, lds, stream>>>(p);
     return hipGetLastError();
+}
+
+// Slots of token t's K entries when the whole batch is one chunk
+// (T * K <= kChunkEntries), found by one workgroup of NT threads without the
+// slot walk.  An entry's row inside its rank's slice is the aligned counts of
+// the rank's experts below its own expert (the expert offset) plus the
+// number of entries naming the same expert earlier in token-then-top-k
+// order; that is the slot the walk assigns, so both agree exactly.  Returns
+// slot j in lane j of every wave (j < K), as slot_of reads it.  s_hist holds
+// E ints, s_part (NT / 64) * EP_MAX_TOPK.  Contains barriers.
+template <int NT>
+__device__ int32_t token_slots_one_chunk(const LayoutParams &p, int t, int *s_hist, int *s_part) {
+    constexpr int kPer = kChunkEntries / NT;
+    constexpr int kWaves = NT / 64;
+    const int n = p.T * p.K;
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
+    const int32_t *trow = p.topk_idx + static_cast<int64_t>(t) * p.K;
+    const int lane_id = trow[min(lane, p.K - 1)];
+    int ids[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) ids[k] = p.topk_idx[min(tid + k * NT, n - 1)];
+    for (int i = tid; i < p.E; i += NT) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (tid + k * NT < n && valid_id(ids[k], p.E)) atomicAdd(&s_hist[ids[k]], 1);
+    __syncthreads();
+    for (int j = 0; j < p.K; ++j) {
+        const int e = __builtin_amdgcn_readlane(lane_id, j);
+        int part = 0;
+        if (valid_id(e, p.E)) {
+            const int lim = t * p.K + j;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) part += (tid + k * NT < lim && ids[k] == e) ? 1 : 0;
+            for (int l = static_cast<int>(p.div_L(e)) * p.L + tid; l < e; l += NT)
+                part += align_up(s_hist[l], p.A);
+        }
+        part = wave_inclusive_sum(part);
+        if (lane == 63) s_part[w * EP_MAX_TOPK + j] = part;
+    }
+    __syncthreads();
+    const int j = min(lane, p.K - 1);
+    int pos = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) pos += s_part[ww * EP_MAX_TOPK + j];
+    return valid_id(lane_id, p.E) && pos < p.S ? static_cast<int32_t>(p.div_L(lane_id)) * p.S + pos : -1;
+}
+
+// Layout and dispatch in one launch for a batch that is one chunk, on a
+// (T, splits + 1) grid.  Workgroup (0, 0), dispatched first, computes and
+// writes the layout except the slots (counts, token-to-rank map, offsets,
+// rank rows, status); the rest of row y = 0 has nothing to do.  Workgroup
+// (t, y > 0) finds the slots of token t itself, writes them to token_slot if
+// y == 1, and dispatches column run y - 1 of the token's row.  Token t's
+// workgroups have the linear ids, and so the XCDs, that dispatch_kernel
+// gives them, which the combine's grid shares: rows a small batch leaves in
+// an XCD's L2 are read back there.
+template <int VPT>
+__global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutParams p, CopyParams c,
+                                                                       DispatchArgs a) {
+    extern __shared__ __align__(16) int smem[];
+    __shared__ int s_part[(kCopyThreads / 64) * EP_MAX_TOPK];
+    if (blockIdx.y == 0) {
+        if (blockIdx.x == 0) assign_chunk<kCopyThreads / 64, kFusedChunk, false>(p, 0);
+        return;
+    }
+    const int t = blockIdx.x;
+    const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
+    u32x4 buf[VPT];
+    load_token_row<VPT>(c, a, t, v0, buf);
+    const int32_t lane_slot = token_slots_one_chunk<kCopyThreads>(p, t, smem, s_part);
+    const bool meta = blockIdx.y == 1;
+    if (meta && static_cast<int>(threadIdx.x) < p.K)
+        p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
+    store_token_rows<VPT>(c, a, t, v0, meta, lane_slot, buf);
 }
 
 }  // namespace
@@ -603,6 +695,40 @@ hipError_t launch_layout(const LayoutParams &p, hipStream_t stream) {
     if (p.E <= 512) return launch_assign<16>(p, stream);
     if (p.E <= 1024) return launch_assign<8>(p, stream);
     return launch_assign<4>(p, stream);
+}
+
+hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, const DispatchArgs &a,
+                                  hipStream_t stream) {
+    if (p.nchunks != 1 || p.T == 0) {
+        const hipError_t err = launch_layout(p, stream);
+        if (err != hipSuccess || p.T == 0) return err;
+        return launch_dispatch(c, a, stream);
+    }
+    int32_t splits, vpt;
+    copy_grid(c.T, c.nvec, &splits, &vpt);
+    CopyParams cp = c;
+    cp.vpt = vpt;
+    const dim3 grid(c.T, splits + 1);
+    // LDS: the layout workgroup's ids, histogram and aligned scan; the
+    // dispatch workgroups' histogram fits inside
+    const size_t lds = sizeof(int) * (kChunkEntries + p.pitch + p.E + 1);
+    switch (vpt) {
+#define EP_LAYOUT_DISPATCH_CASE(V)                                                 \
+    case V:                                                                        \
+        layout_dispatch_kernel<V><<<grid, kCopyThreads, lds, stream>>>(p, cp, a);  \
+        break;
+        EP_LAYOUT_DISPATCH_CASE(1)
+        EP_LAYOUT_DISPATCH_CASE(2)
+        EP_LAYOUT_DISPATCH_CASE(3)
+        EP_LAYOUT_DISPATCH_CASE(4)
+        EP_LAYOUT_DISPATCH_CASE(5)
+        EP_LAYOUT_DISPATCH_CASE(6)
+        EP_LAYOUT_DISPATCH_CASE(7)
+        EP_LAYOUT_DISPATCH_CASE(8)
+#undef EP_LAYOUT_DISPATCH_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace epget

@@ -159,6 +159,25 @@ int ep_dispatch(const ep_problem *problem, const uint16_t *x,
                 uint16_t *recv_x, int32_t *recv_src_token, float *recv_weight,
                 void *stream);
 
+/* Layout then dispatch in one call: the effect of ep_get_layout followed by
+ * ep_dispatch on the same stream, with the arguments, outputs, errors and
+ * status of both.  [SYM] §6.1 feeds the layout's prefix sums and slots
+ * straight into the dispatch launch; here, when the batch is small enough
+ * for one layout chunk (T*K <= 1024 after rounding to whole tokens: decode-
+ * sized batches), both run as a single kernel in which every dispatching
+ * workgroup derives its own token's slots, which saves a launch on the
+ * latency-bound path.  Larger batches run the two calls' kernels in turn.
+ * token_slot is written as ep_get_layout writes it. */
+int ep_layout_dispatch(const ep_problem *problem, const int32_t *topk_idx,
+                       int32_t *expert_count, int32_t *expert_offset,
+                       int32_t *rank_row_count, int32_t *rank_token_count,
+                       int32_t *group_token_count, uint8_t *is_token_in_rank,
+                       int32_t *token_slot, int64_t *cumulative_expert_recv,
+                       void *workspace, size_t workspace_bytes,
+                       const uint16_t *x, const float *topk_weights,
+                       uint16_t *recv_x, int32_t *recv_src_token,
+                       float *recv_weight, void *stream);
+
 /* Combine: out[t,h] = bf16(sum_{j<K} w[t,j] * y[token_slot[t,j], h]), with an
  * fp32 accumulator folded in ascending j by fused multiply-add and one
  * round-to-nearest-even to bf16 — the top-k-weighted reduction that [SYM]

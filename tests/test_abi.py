@@ -101,3 +101,20 @@ def test_fp8_argument_checks():
     assert lib.ep_dispatch_fp8(ctypes.byref(p), a, a, a, a, a, a, 0, 1, a, a, None) == ep.EP_ERR_INVALID_ARG
     # misaligned fp8 rows
     assert lib.ep_dispatch_fp8(ctypes.byref(p), a + 8, a, a, a, a, a, 56, 1, a, a, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_layout_dispatch_argument_checks():
+    """The fused call checks the arguments of both calls it stands for."""
+    p = P()
+    lib = ep.load()
+    a = 1 << 20
+    need = ep.ep_workspace_bytes(p)
+    lay = [a] * 8
+    # small workspace (a layout argument)
+    assert lib.ep_layout_dispatch(ctypes.byref(p), *lay, None, a, need - 1,
+                                  a, a, a, a, a, None) == ep.EP_ERR_INVALID_ARG
+    # misaligned x and NULL recv_x (dispatch arguments)
+    assert lib.ep_layout_dispatch(ctypes.byref(p), *lay, None, a, need,
+                                  a + 2, a, a, a, a, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_layout_dispatch(ctypes.byref(p), *lay, None, a, need,
+                                  a, a, None, a, a, None) == ep.EP_ERR_INVALID_ARG
