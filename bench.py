@@ -34,10 +34,11 @@ PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E peak, GB/s (1e9 bytes)
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 # the sources each kernel family is built from (its code and its launch); a
 # counter record is valid only while these files are unchanged
+_CSRC = "combine_ep_get_amd/csrc/"
 KERNEL_SOURCES = {
-    "layout": ["combine_ep_get_amd/csrc/layout.hip", "combine_ep_get_amd/csrc/ep_internal.h"],
-    "dispatch": ["combine_ep_get_amd/csrc/rows.hip", "combine_ep_get_amd/csrc/ep_internal.h"],
-    "combine": ["combine_ep_get_amd/csrc/rows.hip", "combine_ep_get_amd/csrc/ep_internal.h"],
+    "layout": [_CSRC + "layout.hip", _CSRC + "device_common.h", _CSRC + "ep_internal.h"],
+    "dispatch": [_CSRC + "rows.hip", _CSRC + "device_common.h", _CSRC + "ep_internal.h"],
+    "combine": [_CSRC + "rows.hip", _CSRC + "device_common.h", _CSRC + "ep_internal.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

@@ -1,7 +1,8 @@
 """The hot path captured in a HIP graph replays correctly.
 
-The three calls enqueue kernels only (no memsets, copies or host syncs), so
-a serving loop can capture layout + dispatch + combine once and replay it.
+The hot calls enqueue kernels only (no memsets, copies or host syncs), so
+a serving loop can capture layout + dispatch + combine (or the one-call
+layout-and-dispatch + combine) once and replay it.
 Each replay is checked against the eager result, with the program's own
 eager work and synchronisations between replays."""
 import numpy as np
@@ -14,8 +15,8 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["decode128", "prefill4k"])
-def test_graph_replay_matches_eager(name):
+@pytest.mark.parametrize("name,fused", [("decode128", False), ("prefill4k", False), ("decode128", True)])
+def test_graph_replay_matches_eager(name, fused):
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
     import combine_ep_get_amd as ep
@@ -35,8 +36,11 @@ def test_graph_replay_matches_eager(name):
     out = torch.empty_like(d_x)
 
     def step():
-        ep.ep_get_layout(p, d_idx, *bufs.args())
-        ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, None, None)
+        if fused:
+            ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv, None, None)
+        else:
+            ep.ep_get_layout(p, d_idx, *bufs.args())
+            ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, None, None)
         ep.ep_combine(p, recv, bufs.token_slot, d_w, out)
 
     # eager reference (also warms up)
