@@ -34,6 +34,8 @@
 // Every global read a step needs is issued as one batch of independent loads
 // (indices clamped into range, a buffer load's range check where a predicate
 // is needed), so each step costs about one memory round trip.
+#include <algorithm>
+
 #include "../../include/ep_get.h"
 #include "device_common.h"
 
@@ -601,48 +603,54 @@ hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
 
 // Slots of token t's K entries when the whole batch is one chunk
 // (T * K <= kChunkEntries), found by one workgroup of NT threads without the
-// slot walk.  An entry's row inside its rank's slice is the aligned counts of
-// the rank's experts below its own expert (the expert offset) plus the
-// number of entries naming the same expert earlier in token-then-top-k
-// order; that is the slot the walk assigns, so both agree exactly.  Returns
-// slot j in lane j of every wave (j < K), as slot_of reads it.  s_hist holds
-// E ints, s_part (NT / 64) * EP_MAX_TOPK.  Contains barriers.
+// slot walk.  Entry (t, j) with expert e lands at row
+//   expert_offset[e] + #{entries before (t, j) naming e}
+// of its rank's slice, which is the slot the walk assigns.  The workgroup
+// builds two LDS histograms of the batch, one over all entries and one over
+// the entries of tokens before t, and scans the first into the aligned
+// offsets; the count of earlier entries is the second histogram plus the
+// earlier duplicates of e inside the token.  Returns slot j in lane j of
+// every wave (j < K), as slot_of reads it.  lds holds 3 * E + 2 ints,
+// s_wsum 2 * NT / 64.  Contains barriers.
 template <int NT>
-__device__ int32_t token_slots_one_chunk(const LayoutParams &p, int t, int *s_hist, int *s_part) {
+__device__ int32_t token_slots_one_chunk(const LayoutParams &p, int t, int *lds, int *s_wsum) {
     constexpr int kPer = kChunkEntries / NT;
-    constexpr int kWaves = NT / 64;
+    constexpr int kEPT = (EP_MAX_EXPERTS + NT - 1) / NT;
     const int n = p.T * p.K;
-    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
+    const int tid = threadIdx.x, lane = __lane_id();
+    int *s_all = lds;                   // E + 1: counts, then their exclusive scan
+    int *s_aln = s_all + (p.E + 1);     // E + 1: exclusive scan of aligned counts
+    int *s_before = s_aln + (p.E + 1);  // E: counts over tokens before t
     const int32_t *trow = p.topk_idx + static_cast<int64_t>(t) * p.K;
     const int lane_id = trow[min(lane, p.K - 1)];
     int ids[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) ids[k] = p.topk_idx[min(tid + k * NT, n - 1)];
-    for (int i = tid; i < p.E; i += NT) s_hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-        if (tid + k * NT < n && valid_id(ids[k], p.E)) atomicAdd(&s_hist[ids[k]], 1);
-    __syncthreads();
-    for (int j = 0; j < p.K; ++j) {
-        const int e = __builtin_amdgcn_readlane(lane_id, j);
-        int part = 0;
-        if (valid_id(e, p.E)) {
-            const int lim = t * p.K + j;
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) part += (tid + k * NT < lim && ids[k] == e) ? 1 : 0;
-            for (int l = static_cast<int>(p.div_L(e)) * p.L + tid; l < e; l += NT)
-                part += align_up(s_hist[l], p.A);
-        }
-        part = wave_inclusive_sum(part);
-        if (lane == 63) s_part[w * EP_MAX_TOPK + j] = part;
+    for (int i = tid; i < p.E; i += NT) {
+        s_all[i] = 0;
+        s_before[i] = 0;
     }
     __syncthreads();
-    const int j = min(lane, p.K - 1);
-    int pos = 0;
+    const int first = t * p.K;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) pos += s_part[ww * EP_MAX_TOPK + j];
-    return valid_id(lane_id, p.E) && pos < p.S ? static_cast<int32_t>(p.div_L(lane_id)) * p.S + pos : -1;
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * NT;
+        if (i < n && valid_id(ids[k], p.E)) {
+            atomicAdd(&s_all[ids[k]], 1);
+            if (i < first) atomicAdd(&s_before[ids[k]], 1);
+        }
+    }
+    __syncthreads();
+    block_scan_counts<NT, kEPT>(p, s_all, s_aln, s_all, s_wsum);
+    __syncthreads();
+    const int j = min(lane, p.K - 1);
+    int dup = 0;
+    for (int jj = 0; jj < p.K; ++jj)
+        dup += (jj < j && __builtin_amdgcn_readlane(lane_id, jj) == lane_id) ? 1 : 0;
+    if (!valid_id(lane_id, p.E)) return -1;
+    const int rank = static_cast<int>(p.div_L(lane_id));
+    const int pos = s_aln[lane_id] - s_aln[rank * p.L] + s_before[lane_id] + dup;
+    return pos < p.S ? rank * p.S + pos : -1;
 }
 
 // Layout and dispatch in one launch for a batch that is one chunk, on a
@@ -658,7 +666,7 @@ template <int VPT>
 __global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutParams p, CopyParams c,
                                                                        DispatchArgs a) {
     extern __shared__ __align__(16) int smem[];
-    __shared__ int s_part[(kCopyThreads / 64) * EP_MAX_TOPK];
+    __shared__ int s_wsum[2 * kCopyThreads / 64];
     if (blockIdx.y == 0) {
         if (blockIdx.x == 0) assign_chunk<kCopyThreads / 64, kFusedChunk, false>(p, 0);
         return;
@@ -667,7 +675,7 @@ __global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutPar
     const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
     load_token_row<VPT>(c, a, t, v0, buf);
-    const int32_t lane_slot = token_slots_one_chunk<kCopyThreads>(p, t, smem, s_part);
+    const int32_t lane_slot = token_slots_one_chunk<kCopyThreads>(p, t, smem, s_wsum);
     const bool meta = blockIdx.y == 1;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
@@ -709,9 +717,10 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
     CopyParams cp = c;
     cp.vpt = vpt;
     const dim3 grid(c.T, splits + 1);
-    // LDS: the layout workgroup's ids, histogram and aligned scan; the
-    // dispatch workgroups' histogram fits inside
-    const size_t lds = sizeof(int) * (kChunkEntries + p.pitch + p.E + 1);
+    // LDS: the larger of the layout workgroup's (ids, histogram, aligned
+    // scan) and a dispatch workgroup's (two histograms and a scan)
+    const size_t lds = sizeof(int) * std::max<size_t>(kChunkEntries + p.pitch + p.E + 1,
+                                                      3 * static_cast<size_t>(p.E) + 2);
     switch (vpt) {
 #define EP_LAYOUT_DISPATCH_CASE(V)                                                 \
     case V:                                                                        \
