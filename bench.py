@@ -295,41 +295,41 @@ def main():
         gslot = torch.empty((wl.T, G), dtype=torch.int32, device=dev)
         gbuf = torch.empty((G * SG, wl.H), dtype=torch.int16, device=dev)
 
-    def plain_dispatch_call():
-        if args.hier:
-            ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot, stream=stream)
-            ep.ep_dispatch_hier(p, d_x, d_w, bufs.token_slot, gslot, SG, gbuf, recv, recv_src,
-                                recv_w, stream=stream)
-        elif args.fp8:
-            ep.ep_dispatch_fp8(p, d_q, d_sf, d_w, bufs.token_slot, recv_q, recv_sf, nsf, 1,
-                               recv_src, recv_w, stream=stream)
-        else:
-            ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, recv_src, recv_w, stream=stream)
-
-    def layout_call():
-        if not args.fused:
-            ep.ep_get_layout(p, d_idx, *bufs.args(), stream=stream)
-
-    def dispatch_call():  # with --fused, layout and dispatch in one call
+    def make_calls(st):
+        """The step's calls on stream st, marshalled once (bound calls), as
+        (layout, dispatch, combine) lists; with --fused the layout list is
+        empty and the dispatch list holds the one-call layout-and-dispatch."""
+        b = dict(stream=st, bind=True)
+        layout = [] if args.fused else [ep.ep_get_layout(p, d_idx, *bufs.args(), **b)]
         if args.fused:
-            ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv, recv_src, recv_w,
-                                  stream=stream)
+            dispatch = [ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv, recv_src,
+                                              recv_w, **b)]
+        elif args.hier:
+            dispatch = [ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot, **b),
+                        ep.ep_dispatch_hier(p, d_x, d_w, bufs.token_slot, gslot, SG, gbuf, recv,
+                                            recv_src, recv_w, **b)]
+        elif args.fp8:
+            dispatch = [ep.ep_dispatch_fp8(p, d_q, d_sf, d_w, bufs.token_slot, recv_q, recv_sf, nsf, 1,
+                                           recv_src, recv_w, **b)]
         else:
-            plain_dispatch_call()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        layout_call()
-        if ev is not None:
-            ev[1].record(stream)
-        dispatch_call()
-        if ev is not None:
-            ev[2].record(stream)
+            dispatch = [ep.ep_dispatch(p, d_x, d_w, bufs.token_slot, recv, recv_src, recv_w, **b)]
         if args.hier:
-            ep.ep_combine_hier(p, recv, bufs.token_slot, d_w, gslot, SG, gbuf, out, stream=stream)
+            combine = [ep.ep_combine_hier(p, recv, bufs.token_slot, d_w, gslot, SG, gbuf, out, **b)]
         else:
-            ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
+            combine = [ep.ep_combine(p, recv, bufs.token_slot, d_w, out, **b)]
+        return layout, dispatch, combine
+
+    phases = make_calls(stream)
+
+    def run(calls):
+        for f in calls:
+            f()
+
+    def step(ev=None, calls=phases):
+        for k, part in enumerate(calls):
+            if ev is not None:
+                ev[k].record(stream)
+            run(part)
         if ev is not None:
             ev[3].record(stream)
 
@@ -347,11 +347,10 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         torch.cuda.synchronize()
+        side_calls = make_calls(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
-            stream_saved, stream = stream, side
-            step()
-            stream = stream_saved
+            step(calls=side_calls)
         torch.cuda.synchronize()
         run_step = graph.replay
 
@@ -391,21 +390,11 @@ def main():
         torch.cuda.synchronize()
         for i in range(args.steps):
             ev = cold_ev[i]
-            scratch.fill_(i & 0xFF)
-            ev[0].record(stream)
-            layout_call()
-            ev[1].record(stream)
-            scratch.fill_((i + 1) & 0xFF)
-            ev[2].record(stream)
-            dispatch_call()
-            ev[3].record(stream)
-            scratch.fill_((i + 2) & 0xFF)
-            ev[4].record(stream)
-            if args.hier:
-                ep.ep_combine_hier(p, recv, bufs.token_slot, d_w, gslot, SG, gbuf, out, stream=stream)
-            else:
-                ep.ep_combine(p, recv, bufs.token_slot, d_w, out, stream=stream)
-            ev[5].record(stream)
+            for k, part in enumerate(phases):
+                scratch.fill_((i + k) & 0xFF)
+                ev[2 * k].record(stream)
+                run(part)
+                ev[2 * k + 1].record(stream)
         torch.cuda.synchronize()
         cold_us = {
             "layout": float(np.mean([e[0].elapsed_time(e[1]) for e in cold_ev])) * 1e3,

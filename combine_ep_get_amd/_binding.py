@@ -134,6 +134,29 @@ def _check(rc: int, where: str) -> int:
     return rc
 
 
+class BoundCall:
+    """One entry point with its arguments marshalled once.  Calling it issues
+    the same C call again (same pointers, sizes and stream), so a loop that
+    repeats a step pays only for the call itself.  The tensors must stay
+    alive and in place while it is used; the problem struct is passed by
+    reference, so later changes to it are seen."""
+
+    def __init__(self, name: str, args: tuple):
+        self.name = name
+        self._fn = getattr(load(), name)
+        self._args = args
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._args), self.name)
+
+
+def _run(name: str, args: tuple, bind: bool):
+    """Calls the entry point now, or with bind=True returns it as a BoundCall."""
+    if bind:
+        return BoundCall(name, args)
+    return _check(getattr(load(), name)(*args), name)
+
+
 def ep_workspace_bytes(problem: Problem) -> int:
     return load().ep_workspace_bytes(ctypes.byref(problem))
 
@@ -144,91 +167,81 @@ def ep_rank_stride_hint(problem: Problem) -> int:
 
 def ep_get_layout(problem, topk_idx, expert_count, expert_offset, rank_row_count,
                   rank_token_count, group_token_count, is_token_in_rank, token_slot,
-                  cumulative_expert_recv, workspace, workspace_bytes=None, stream=None) -> int:
+                  cumulative_expert_recv, workspace, workspace_bytes=None, stream=None, bind=False):
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    rc = load().ep_get_layout(ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
-                              _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
-                              _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
-                              _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
-                              _stream(stream))
-    return _check(rc, "ep_get_layout")
+    return _run("ep_get_layout", (ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
+                                  _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
+                                  _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
+                                  _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
+                                  _stream(stream)), bind)
 
 
 def ep_dispatch(problem, x, topk_weights, token_slot, recv_x, recv_src_token=None,
-                recv_weight=None, stream=None) -> int:
-    rc = load().ep_dispatch(ctypes.byref(problem), _ptr(x), _ptr(topk_weights), _ptr(token_slot),
-                            _ptr(recv_x), _ptr(recv_src_token), _ptr(recv_weight), _stream(stream))
-    return _check(rc, "ep_dispatch")
+                recv_weight=None, stream=None, bind=False):
+    return _run("ep_dispatch", (ctypes.byref(problem), _ptr(x), _ptr(topk_weights), _ptr(token_slot),
+                                _ptr(recv_x), _ptr(recv_src_token), _ptr(recv_weight), _stream(stream)), bind)
 
 
 def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_count,
                        rank_token_count, group_token_count, is_token_in_rank, token_slot,
                        cumulative_expert_recv, workspace, workspace_bytes, x, topk_weights, recv_x,
-                       recv_src_token=None, recv_weight=None, stream=None) -> int:
+                       recv_src_token=None, recv_weight=None, stream=None, bind=False):
     """ep_get_layout followed by ep_dispatch (one kernel for decode-sized batches)."""
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    rc = load().ep_layout_dispatch(ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
-                                   _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
-                                   _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
-                                   _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
-                                   _ptr(x), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_src_token),
-                                   _ptr(recv_weight), _stream(stream))
-    return _check(rc, "ep_layout_dispatch")
+    return _run("ep_layout_dispatch", (ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
+                                       _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
+                                       _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
+                                       _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
+                                       _ptr(x), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_src_token),
+                                       _ptr(recv_weight), _stream(stream)), bind)
 
 
-def ep_combine(problem, y, token_slot, topk_weights, out, stream=None) -> int:
-    rc = load().ep_combine(ctypes.byref(problem), _ptr(y), _ptr(token_slot), _ptr(topk_weights),
-                           _ptr(out), _stream(stream))
-    return _check(rc, "ep_combine")
+def ep_combine(problem, y, token_slot, topk_weights, out, stream=None, bind=False):
+    return _run("ep_combine", (ctypes.byref(problem), _ptr(y), _ptr(token_slot), _ptr(topk_weights),
+                               _ptr(out), _stream(stream)), bind)
 
 
-def ep_quantize_fp8(problem, x, x_fp8, x_sf, stream=None) -> int:
-    rc = load().ep_quantize_fp8(ctypes.byref(problem), _ptr(x), _ptr(x_fp8), _ptr(x_sf),
-                                _stream(stream))
-    return _check(rc, "ep_quantize_fp8")
+def ep_quantize_fp8(problem, x, x_fp8, x_sf, stream=None, bind=False):
+    return _run("ep_quantize_fp8", (ctypes.byref(problem), _ptr(x), _ptr(x_fp8), _ptr(x_sf),
+                                    _stream(stream)), bind)
 
 
 def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, recv_sf,
                     sf_token_stride, sf_hidden_stride, recv_src_token=None, recv_weight=None,
-                    stream=None) -> int:
-    rc = load().ep_dispatch_fp8(ctypes.byref(problem), _ptr(x_fp8), _ptr(x_sf), _ptr(topk_weights),
-                                _ptr(token_slot), _ptr(recv_x_fp8), _ptr(recv_sf),
-                                sf_token_stride, sf_hidden_stride, _ptr(recv_src_token),
-                                _ptr(recv_weight), _stream(stream))
-    return _check(rc, "ep_dispatch_fp8")
+                    stream=None, bind=False):
+    return _run("ep_dispatch_fp8", (ctypes.byref(problem), _ptr(x_fp8), _ptr(x_sf), _ptr(topk_weights),
+                                    _ptr(token_slot), _ptr(recv_x_fp8), _ptr(recv_sf),
+                                    sf_token_stride, sf_hidden_stride, _ptr(recv_src_token),
+                                    _ptr(recv_weight), _stream(stream)), bind)
 
 
 def ep_get_group_layout(problem, is_token_in_rank, group_stride_rows, group_slot,
-                        stream=None) -> int:
-    rc = load().ep_get_group_layout(ctypes.byref(problem), _ptr(is_token_in_rank),
-                                    group_stride_rows, _ptr(group_slot), _stream(stream))
-    return _check(rc, "ep_get_group_layout")
+                        stream=None, bind=False):
+    return _run("ep_get_group_layout", (ctypes.byref(problem), _ptr(is_token_in_rank),
+                                        group_stride_rows, _ptr(group_slot), _stream(stream)), bind)
 
 
 def ep_dispatch_hier(problem, x, topk_weights, token_slot, group_slot, group_stride_rows,
-                     group_buf, recv_x, recv_src_token=None, recv_weight=None, stream=None) -> int:
-    rc = load().ep_dispatch_hier(ctypes.byref(problem), _ptr(x), _ptr(topk_weights),
-                                 _ptr(token_slot), _ptr(group_slot), group_stride_rows,
-                                 _ptr(group_buf), _ptr(recv_x), _ptr(recv_src_token),
-                                 _ptr(recv_weight), _stream(stream))
-    return _check(rc, "ep_dispatch_hier")
+                     group_buf, recv_x, recv_src_token=None, recv_weight=None, stream=None, bind=False):
+    return _run("ep_dispatch_hier", (ctypes.byref(problem), _ptr(x), _ptr(topk_weights),
+                                     _ptr(token_slot), _ptr(group_slot), group_stride_rows,
+                                     _ptr(group_buf), _ptr(recv_x), _ptr(recv_src_token),
+                                     _ptr(recv_weight), _stream(stream)), bind)
 
 
 def ep_combine_hier(problem, y, token_slot, topk_weights, group_slot, group_stride_rows,
-                    group_buf, out, stream=None) -> int:
-    rc = load().ep_combine_hier(ctypes.byref(problem), _ptr(y), _ptr(token_slot),
-                                _ptr(topk_weights), _ptr(group_slot), group_stride_rows,
-                                _ptr(group_buf), _ptr(out), _stream(stream))
-    return _check(rc, "ep_combine_hier")
+                    group_buf, out, stream=None, bind=False):
+    return _run("ep_combine_hier", (ctypes.byref(problem), _ptr(y), _ptr(token_slot),
+                                    _ptr(topk_weights), _ptr(group_slot), group_stride_rows,
+                                    _ptr(group_buf), _ptr(out), _stream(stream)), bind)
 
 
 def ep_combine_topk_weights(problem, recv_weight, token_slot, combined_topk_weights,
-                            stream=None) -> int:
-    rc = load().ep_combine_topk_weights(ctypes.byref(problem), _ptr(recv_weight), _ptr(token_slot),
-                                        _ptr(combined_topk_weights), _stream(stream))
-    return _check(rc, "ep_combine_topk_weights")
+                            stream=None, bind=False):
+    return _run("ep_combine_topk_weights", (ctypes.byref(problem), _ptr(recv_weight), _ptr(token_slot),
+                                            _ptr(combined_topk_weights), _stream(stream)), bind)
 
 
 def ep_read_status(workspace, stream=None) -> int:

@@ -207,27 +207,36 @@ __device__ void token_pass(const LayoutParams &p, int t0, int t1, const int *s_i
 }
 
 // Exclusive scans over all experts of the aligned and raw counts by the
-// whole workgroup: thread t sums experts [t*EPT, (t+1)*EPT), a DPP wave scan
-// combines the threads of a wave, and the wave totals go through LDS.
-// s_aln and s_raw get E+1 entries (the last one is the total).  `counts` may
-// be the same LDS array as s_raw: every thread reads its experts before the
-// barrier that precedes the writes.  Contains barriers: call from the whole
-// workgroup.
+// whole workgroup: thread t sums the ept = ceil(E / NT) <= EPT experts
+// [t*ept, (t+1)*ept), a DPP wave scan combines the threads of a wave, and the
+// wave totals go through LDS.  s_aln and s_raw get E+1 entries (the last one
+// is the total).  `counts` may be the same LDS array as s_raw: every thread
+// reads its experts before the barrier that precedes the writes.  Contains
+// barriers: call from the whole workgroup.
 template <int NT, int EPT>
 __device__ void block_scan_counts(const LayoutParams &p, const int *counts, int *s_aln,
                                   int *s_raw, int *s_wsum) {
     constexpr int kWavesPerBlock = NT / 64;
     const int lane = __lane_id(), w = threadIdx.x >> 6;
-    const int e0 = threadIdx.x * EPT;
+    const int ept = (p.E + NT - 1) / NT;
+    const int e0 = threadIdx.x * ept;
     int ca[EPT], cr[EPT];
     int sa = 0, sr = 0;
 #pragma unroll
+    for (int k = 0; k < EPT; ++k) cr[k] = k < ept && e0 + k < p.E ? counts[e0 + k] : 0;
+    // A is uniform: branch once instead of selecting per expert (the
+    // generic division would otherwise run for every count)
+    if (p.A == 1) {
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) ca[k] = cr[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) ca[k] = align_up(cr[k], p.A);
+    }
+#pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        const int c = e0 + k < p.E ? counts[e0 + k] : 0;
-        cr[k] = c;
-        ca[k] = align_up(c, p.A);
         sa += ca[k];
-        sr += c;
+        sr += cr[k];
     }
     const int ia = wave_inclusive_sum(sa), ir = wave_inclusive_sum(sr);
     if (lane == 63) {
@@ -247,7 +256,7 @@ __device__ void block_scan_counts(const LayoutParams &p, const int *counts, int 
     int ea = pa + ia - sa, er = pr + ir - sr;
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        if (e0 + k < p.E) {
+        if (k < ept && e0 + k < p.E) {
             s_aln[e0 + k] = ea;
             s_raw[e0 + k] = er;
         }
@@ -391,6 +400,12 @@ enum AssignMode {
     kScannedTable = 2  // reads the bases and totals pass 2 wrote
 };
 
+// What a fused-chunk workgroup computes: everything, or one of two halves
+// that two workgroups run side by side (the per-token half: the token-to-rank
+// map and unique tokens per rank and group; the per-expert half: counts,
+// offsets, rank rows and the status).
+enum LayoutPart { kLayoutAll = 0, kLayoutExperts = 1, kLayoutTokens = 2 };
+
 // Experts each thread of a W-wave assign workgroup scans.
 template <int W>
 constexpr int assign_experts_per_thread() {
@@ -406,7 +421,7 @@ constexpr int assign_experts_per_thread() {
 // LDS: s_idx [kChunkEntries] | fused: s_hist [pitch], whose expert columns
 // later hold the raw scan; otherwise s_raw [E+1] | s_aln [E+1] | s_wave [W*E]
 // (s_wave only with kWalk).
-template <int W, int kMode, bool kWalk>
+template <int W, int kMode, bool kWalk, int kPart = kLayoutAll>
 __device__ void assign_chunk(const LayoutParams &p, int c) {
     constexpr bool kFused = kMode == kFusedChunk;
     constexpr int NT = 64 * W;
@@ -514,22 +529,29 @@ __device__ void assign_chunk(const LayoutParams &p, int c) {
     }
 
     // 2. per-wave expert counts (and, fused, the whole histogram)
-    entry_pass<NT>(p, n, W, s_idx, kFused ? s_hist : nullptr, kWalk ? s_wave : nullptr);
+    static_assert(kPart == kLayoutAll || (kFused && !kWalk), "split layouts are fused-chunk only");
+    constexpr bool kExperts = kPart != kLayoutTokens, kTokens = kPart != kLayoutExperts;
+    entry_pass<NT>(p, n, W, s_idx, kFused && kExperts ? s_hist : nullptr, kWalk ? s_wave : nullptr);
     __syncthreads();
     if (kFused) {
-        token_pass<NT>(p, t0, t1, s_idx, s_hist);
+        if (kTokens) token_pass<NT>(p, t0, t1, s_idx, s_hist);
         __syncthreads();
         for (int i = tid; i < p.E + p.R + p.G; i += NT) {
             const int v = s_hist[i];
             if (i < p.E) {
-                p.expert_count[i] = v;
-                if (p.cumulative) p.cumulative[i] += v;
+                if (kExperts) {
+                    p.expert_count[i] = v;
+                    if (p.cumulative) p.cumulative[i] += v;
+                }
+            } else if (!kTokens) {
+                continue;
             } else if (i < p.E + p.R) {
                 p.rank_token_count[i - p.E] = v;
             } else if (p.group_token_count) {
                 p.group_token_count[i - p.E - p.R] = v;
             }
         }
+        if (!kExperts) return;  // the whole workgroup, after its last barrier
         __syncthreads();  // s_hist's expert columns become s_raw below
     }
     if (kFused) bad = s_hist[p.E + p.R + p.G];
@@ -654,9 +676,11 @@ __device__ int32_t token_slots_one_chunk(const LayoutParams &p, int t, int *lds,
 }
 
 // Layout and dispatch in one launch for a batch that is one chunk, on a
-// (T, splits + 1) grid.  Workgroup (0, 0), dispatched first, computes and
-// writes the layout except the slots (counts, token-to-rank map, offsets,
-// rank rows, status); the rest of row y = 0 has nothing to do.  Workgroup
+// (T, splits + 1) grid.  Workgroups (0, 0) and (1, 0), dispatched first,
+// compute and write the layout except the slots: the per-expert half
+// (counts, offsets, rank rows, status) and the per-token half (token-to-rank
+// map, unique tokens per rank and group); the rest of row y = 0 has nothing
+// to do.  Workgroup
 // (t, y > 0) finds the slots of token t itself, writes them to token_slot if
 // y == 1, and dispatches column run y - 1 of the token's row.  Token t's
 // workgroups have the linear ids, and so the XCDs, that dispatch_kernel
@@ -668,7 +692,14 @@ __global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutPar
     extern __shared__ __align__(16) int smem[];
     __shared__ int s_wsum[2 * kCopyThreads / 64];
     if (blockIdx.y == 0) {
-        if (blockIdx.x == 0) assign_chunk<kCopyThreads / 64, kFusedChunk, false>(p, 0);
+        // the layout, split over workgroups (0, 0) and (1, 0) when there are two
+        constexpr int W = kCopyThreads / 64;
+        if (gridDim.x == 1)
+            assign_chunk<W, kFusedChunk, false, kLayoutAll>(p, 0);
+        else if (blockIdx.x == 0)
+            assign_chunk<W, kFusedChunk, false, kLayoutExperts>(p, 0);
+        else if (blockIdx.x == 1)
+            assign_chunk<W, kFusedChunk, false, kLayoutTokens>(p, 0);
         return;
     }
     const int t = blockIdx.x;

@@ -355,3 +355,35 @@ def test_repeatable(ep):
         _, bufs, _ = gpu_layout(ep, inp.topk_idx, wl.E, wl.R, S)
         outs.append(bufs.token_slot.cpu().numpy())
     assert all((o == outs[0]).all() for o in outs)
+
+
+def test_bound_calls_repeat_the_direct_calls(ep):
+    """Calls marshalled once (bind=True) give the direct calls' results, and
+    repeating them repeats the work."""
+    inp = ep_inputs.make_inputs("decode128")
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, wl.A, S)
+    rows = wl.R * S
+    d_idx, d_x, d_w = dev(inp.topk_idx), bf16_dev(inp.x), dev(inp.topk_weights)
+    a, b = ep.alloc_layout(p, cumulative=True), ep.alloc_layout(p, cumulative=True)
+    ra = torch.zeros((rows, wl.H), dtype=torch.int16, device="cuda")
+    rb = torch.zeros_like(ra)
+    oa = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+    ob = torch.empty_like(oa)
+    calls = [ep.ep_get_layout(p, d_idx, *a.args(), bind=True),
+             ep.ep_dispatch(p, d_x, d_w, a.token_slot, ra, bind=True),
+             ep.ep_combine(p, ra, a.token_slot, d_w, oa, bind=True)]
+    for _ in range(2):
+        for f in calls:
+            f()
+        ep.ep_get_layout(p, d_idx, *b.args())
+        ep.ep_dispatch(p, d_x, d_w, b.token_slot, rb)
+        ep.ep_combine(p, rb, b.token_slot, d_w, ob)
+    torch.cuda.synchronize()
+    assert torch.equal(a.token_slot, b.token_slot)
+    assert torch.equal(ra, rb)
+    assert torch.equal(oa, ob)
+    # the cumulative counter saw both bound layouts
+    assert torch.equal(a.cumulative_expert_recv, 2 * a.expert_count.to(torch.int64))
+    assert torch.equal(a.cumulative_expert_recv, b.cumulative_expert_recv)
