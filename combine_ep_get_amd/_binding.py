@@ -23,6 +23,7 @@ EP_MAX_RANKS = 1024
 EP_MAX_EXPERTS = 2048
 EP_MAX_EXPERTS_PER_RANK = 256
 EP_MAX_TOPK = 32
+EP_MAX_HIDDEN = 1 << 24
 
 # Every function the C header declares, checked by the test-suite.
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",

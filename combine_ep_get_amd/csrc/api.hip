@@ -22,7 +22,7 @@ int check_shape(const ep_problem *p) {
     if (!p) return EP_ERR_INVALID_ARG;
     if (p->reserved != 0) return EP_ERR_INVALID_ARG;
     if (p->num_tokens < 0) return EP_ERR_INVALID_ARG;
-    if (p->hidden < 8 || p->hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+    if (p->hidden < 8 || p->hidden % 8 != 0 || p->hidden > EP_MAX_HIDDEN) return EP_ERR_INVALID_ARG;
     if (p->num_experts < 1 || p->num_experts > EP_MAX_EXPERTS) return EP_ERR_INVALID_ARG;
     if (p->num_ranks < 1 || p->num_ranks > EP_MAX_RANKS) return EP_ERR_INVALID_ARG;
     if (p->num_experts % p->num_ranks != 0) return EP_ERR_INVALID_ARG;

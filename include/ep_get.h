@@ -58,11 +58,13 @@ extern "C" {
 #define EP_ERR_BAD_EXPERT (-4)  /* an id outside [0,E) other than -1 (device-detected) */
 
 /* Limits of [V2] (kNumMaxRanks, kNumMaxExperts, kNumMaxExpertsPerRank)
- * and this library's own top-k limit. */
+ * and this library's own top-k and hidden-size limits (a row of H bf16
+ * must fit the launch grid: 2^24 channels is a 32 MiB row). */
 #define EP_MAX_RANKS 1024
 #define EP_MAX_EXPERTS 2048
 #define EP_MAX_EXPERTS_PER_RANK 256
 #define EP_MAX_TOPK 32
+#define EP_MAX_HIDDEN (1 << 24)
 
 /* Problem description shared by all calls.  Valid when:
  *   T >= 0; H >= 8 and H % 8 == 0 (rows are whole 16-byte vectors);
@@ -72,7 +74,7 @@ extern "C" {
  *   T * K + E * A <= INT32_MAX. */
 typedef struct ep_problem {
     int32_t num_tokens;       /* T: tokens of this source rank */
-    int32_t hidden;           /* H: bf16 elements per row */
+    int32_t hidden;           /* H: bf16 elements per row, a multiple of 8, <= EP_MAX_HIDDEN */
     int32_t num_experts;      /* E */
     int32_t num_topk;         /* K */
     int32_t num_ranks;        /* R: destination ranks (slices) */

@@ -51,7 +51,7 @@ def test_stride_hint_and_workspace():
 
 @pytest.mark.parametrize("bad", [
     dict(E=255), dict(E=4096, R=8), dict(R=2048, E=2048), dict(E=1024, R=2),   # limits
-    dict(K=0), dict(K=33), dict(H=7), dict(H=0), dict(T=-1), dict(G=3), dict(G=0),
+    dict(K=0), dict(K=33), dict(H=7), dict(H=0), dict(H=(1 << 24) + 8), dict(T=-1), dict(G=3), dict(G=0),
     dict(A=0), dict(S=0), dict(S=2**31 // 8 + 1),
 ])
 def test_invalid_problems_rejected_before_launch(bad):

@@ -267,6 +267,19 @@ def test_random_shapes(ep, seed):
     _case(ep, idx, E, R, G=G, A=A, H=H, seed=seed)
 
 
+@pytest.mark.parametrize("T,H,E,K,R", [
+    (300, 16384, 64, 6, 8),       # 32 KB rows: several workgroups per row in both kernels
+    (17, 65536, 16, 4, 4),        # 128 KB rows
+    (131072, 32, 256, 8, 16),     # 1024 layout chunks: eight rounds of the scan pass
+    (5000, 8, 32, 5, 4),          # one 16-byte vector per row
+])
+def test_wide_rows_and_long_batches(ep, T, H, E, K, R):
+    rng = np.random.default_rng(T + H)
+    idx = _route_uniform(rng, T, E, K)
+    print(f"[parity] T={T} H={H} E={E} K={K} R={R}", flush=True)
+    _case(ep, idx, E, R, H=H, seed=T)
+
+
 def test_large_expert_count_and_rank_count(ep):
     rng = np.random.default_rng(8)
     E, R, K, T = 2048, 1024, 32, 1500
