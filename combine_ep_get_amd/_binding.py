@@ -108,11 +108,14 @@ def load():
 
 
 def _ptr(t):
-    """Device pointer of a tensor, a raw integer address, or NULL for None."""
+    """Device pointer of a tensor, a raw integer address, or NULL for None.
+    The library reads every array densely, so a strided view is refused."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError("libepget takes contiguous arrays; call .contiguous() first")
     return t.data_ptr()
 
 

@@ -30,6 +30,9 @@
 //      itself and pass 2 is skipped.
 // Single-chunk path (one launch, batches of up to kChunkEntries entries): the
 // assign workgroup also builds the histogram and writes the counts.
+// Layout and dispatch in one launch (one-chunk batches): two workgroups
+// write the layout outputs while every dispatching workgroup derives its own
+// token's slots from LDS histograms of the batch (layout_dispatch_kernel).
 //
 // Every global read a step needs is issued as one batch of independent loads
 // (indices clamped into range, a buffer load's range check where a predicate

@@ -7,7 +7,8 @@
 // dispatch ("DeepEP Symmetric Memory 全面架构分析" §6.1 dispatch arguments;
 // the received record of "DeepEP V2 ElasticBuffer 架构深度分析", TokenLayout
 // block): each thread loads its vectors of x[t] once and stores them to all
-// K destination rows — one read, K writes per vector.
+// K destination rows — one read, K writes per vector (the row copy itself is
+// in device_common.h, shared with the one-launch layout and dispatch).
 //
 // combine (same first page, §9.2 combine(x, handle, topk_weights)): each
 // thread gathers the K rows' vectors for one column position (K loads in

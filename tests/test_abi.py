@@ -118,3 +118,12 @@ def test_layout_dispatch_argument_checks():
                                   a + 2, a, a, a, a, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_layout_dispatch(ctypes.byref(p), *lay, None, a, need,
                                   a, a, None, a, a, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_binding_refuses_strided_views():
+    """A transposed or sliced view would be read as if it were dense."""
+    import torch
+    p = P()
+    view = torch.zeros((8, 16), dtype=torch.int16).t()
+    with pytest.raises(ValueError):
+        ep.ep_combine(p, view, 1 << 20, None, 1 << 20, stream=0)
