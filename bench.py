@@ -65,11 +65,20 @@ def algorithmic_bytes(wl, fp8=False):
     return {"layout": lay, "dispatch": dis, "combine": com}
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
