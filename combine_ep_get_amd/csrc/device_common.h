@@ -40,13 +40,15 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // e4m3 codes with per-row scale factors).
 //
 // load_token_row: the thread's vectors of x[t].  Loads are unconditional
-// (the column is clamped into the row) so they issue back to back.
+// (the column is clamped into the row) so they issue back to back; x is read
+// once, so they carry the non-temporal hint (measured about 1 µs faster on a
+// 4096-token step).
 template <int VPT>
 __device__ __forceinline__ void load_token_row(const CopyParams &c, const DispatchArgs &a, int t, int v0,
                                                u32x4 (&buf)[VPT]) {
     const u32x4 *src = static_cast<const u32x4 *>(a.x) + static_cast<int64_t>(t) * c.nvec;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
+    for (int v = 0; v < VPT; ++v) buf[v] = __builtin_nontemporal_load(src + min(v0 + v * kCopyThreads, c.nvec - 1));
 }
 
 // Slot j of the token, held by lane j of every wave (j < K <= 32): a
