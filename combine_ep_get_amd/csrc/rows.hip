@@ -59,21 +59,23 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
 }
 
 // Per-token, per-128-channel e4m3 quantisation: 8 lanes hold a block of 128
-// channels (16 bf16 each: two 16-byte loads, one 16-byte store of codes), so
-// a wave covers 8 blocks and a workgroup of kQuantThreads covers
-// 16 * kQuantThreads channels of one token.
+// channels (16 bf16 each: two 16-byte loads, one 16-byte store of codes).
+// With H a multiple of 128 the blocks of all tokens tile x in order: block p
+// (token p / (H/128), block p % (H/128)) starts at element 128 p and owns
+// scale p, so the grid walks the flat block index and a workgroup of
+// kQuantThreads covers 16 * kQuantThreads consecutive channels of x, with no
+// idle lanes at the row ends.
 constexpr int kQuantThreads = 256;
 constexpr int kQuantLanesPerBlock = 8;
+constexpr int kQuantBlocksPerGroup = kQuantThreads / kQuantLanesPerBlock;
 
-__global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(int32_t H, const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(int64_t nblocks, const uint16_t *__restrict__ x,
                                                                      uint8_t *__restrict__ q,
                                                                      float *__restrict__ sf) {
-    const int t = blockIdx.x;
     const int lane = threadIdx.x % kQuantLanesPerBlock;
-    const int blk = blockIdx.y * (kQuantThreads / kQuantLanesPerBlock) + threadIdx.x / kQuantLanesPerBlock;
-    const int nb = H / 128;
-    const bool live = blk < nb;
-    const int64_t off = static_cast<int64_t>(t) * H + static_cast<int64_t>(min(blk, nb - 1)) * 128 + lane * 16;
+    const int64_t blk = static_cast<int64_t>(blockIdx.x) * kQuantBlocksPerGroup + threadIdx.x / kQuantLanesPerBlock;
+    const bool live = blk < nblocks;
+    const int64_t off = (live ? blk : nblocks - 1) * 128 + lane * 16;
     const u32x4 in0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + off));
     const u32x4 in1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + off) + 1);
     float f[16];
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(int32_t H, 
     }
     if (live) {
         *reinterpret_cast<u32x4 *>(q + off) = codes;
-        if (lane == 0) sf[static_cast<int64_t>(t) * nb + blk] = amax / 448.0f;
+        if (lane == 0) sf[blk] = amax / 448.0f;
     }
 }
 
@@ -383,10 +385,10 @@ hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream
 
 hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, float *sf,
                                hipStream_t stream) {
-    const int nb = H / 128;
-    const int per_block = kQuantThreads / kQuantLanesPerBlock;
-    dim3 grid(T, (nb + per_block - 1) / per_block);
-    quantize_fp8_kernel<<<grid, kQuantThreads, 0, stream>>>(H, x, q, sf);
+    const int64_t nblocks = static_cast<int64_t>(T) * (H / 128);
+    const int64_t groups = (nblocks + kQuantBlocksPerGroup - 1) / kQuantBlocksPerGroup;
+    if (groups > INT32_MAX) return hipErrorInvalidValue;
+    quantize_fp8_kernel<<<static_cast<uint32_t>(groups), kQuantThreads, 0, stream>>>(nblocks, x, q, sf);
     return hipGetLastError();
 }
 
