@@ -29,7 +29,8 @@
 //      kMaxTableSum) each assign workgroup sums the table rows it needs
 //      itself and pass 2 is skipped.
 // Single-chunk path (one launch, batches of up to kChunkEntries entries): the
-// assign workgroup also builds the histogram and writes the counts.
+// assign workgroup also builds the histogram and writes the counts, and a
+// second workgroup writes the token-to-rank map and unique-token counts.
 // Layout and dispatch in one launch (one-chunk batches): two workgroups
 // write the layout outputs while every dispatching workgroup derives its own
 // token's slots from LDS histograms of the batch (layout_dispatch_kernel).
@@ -532,7 +533,8 @@ __device__ void assign_chunk(const LayoutParams &p, int c) {
     }
 
     // 2. per-wave expert counts (and, fused, the whole histogram)
-    static_assert(kPart == kLayoutAll || (kFused && !kWalk), "split layouts are fused-chunk only");
+    static_assert(kPart == kLayoutAll || kFused, "split layouts are fused-chunk only");
+    static_assert(!(kWalk && kPart == kLayoutTokens), "the slot walk belongs to the per-expert half");
     constexpr bool kExperts = kPart != kLayoutTokens, kTokens = kPart != kLayoutExperts;
     entry_pass<NT>(p, n, W, s_idx, kFused && kExperts ? s_hist : nullptr, kWalk ? s_wave : nullptr);
     __syncthreads();
@@ -597,6 +599,17 @@ __global__ __launch_bounds__(64 * W) void layout_assign_kernel(LayoutParams p) {
     assign_chunk<W, kMode, true>(p, blockIdx.x);
 }
 
+// A one-chunk batch on two workgroups: workgroup 0 takes the per-expert half
+// and the slot walk, workgroup 1 the per-token half (token-to-rank map and
+// unique tokens per rank and group), which then leaves the critical path.
+template <int W>
+__global__ __launch_bounds__(64 * W) void layout_one_chunk_kernel(LayoutParams p) {
+    if (blockIdx.x == 0)
+        assign_chunk<W, kFusedChunk, true, kLayoutExperts>(p, 0);
+    else
+        assign_chunk<W, kFusedChunk, false, kLayoutTokens>(p, 0);
+}
+
 // Largest table sum (rows x experts per thread) the assign kernel does itself
 // instead of running pass 2.
 constexpr int kMaxTableSum = 64;
@@ -607,7 +620,7 @@ hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
     constexpr int kEPT = assign_experts_per_thread<W>();
     if (p.nchunks == 1) {
         const size_t lds = sizeof(int) * (kChunkEntries + p.pitch) + tail;
-        layout_assign_kernel<W, kFusedChunk><<<1, 64 * W, lds, stream>>>(p);
+        layout_one_chunk_kernel<W><<<2, 64 * W, lds, stream>>>(p);
         return hipGetLastError();
     }
     const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch);
