@@ -420,7 +420,8 @@ constexpr int assign_experts_per_thread() {
 // writes expert_offset, rank_row_count and the status word (and, unless
 // pass 2 ran, the per-expert / per-rank / per-group counts).  Without kWalk
 // everything but the slots is computed (a fused dispatch derives those per
-// token instead).
+// token instead).  For a one-chunk batch kPart lets two workgroups share the
+// work: the per-expert half (which keeps the walk) and the per-token half.
 //
 // LDS: s_idx [kChunkEntries] | fused: s_hist [pitch], whose expert columns
 // later hold the raw scan; otherwise s_raw [E+1] | s_aln [E+1] | s_wave [W*E]
