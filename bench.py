@@ -231,8 +231,8 @@ def main():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="build profiles/traffic.json from rocprofv3 --pmc counter CSVs (no GPU needed)")
     args = ap.parse_args()
-    if args.fused and (args.fp8 or args.hier):
-        ap.error("--fused applies to the flat bf16 path only")
+    if args.fused and args.hier:
+        ap.error("--fused applies to the flat path only")
 
     # counter records are kept per workload and mode
     traffic_key = args.workload + ("+fp8" if args.fp8 else "") + ("+two-level" if args.hier else "")
@@ -310,7 +310,10 @@ def main():
         empty and the dispatch list holds the one-call layout-and-dispatch."""
         b = dict(stream=st, bind=True)
         layout = [] if args.fused else [ep.ep_get_layout(p, d_idx, *bufs.args(), **b)]
-        if args.fused:
+        if args.fused and args.fp8:
+            dispatch = [ep.ep_layout_dispatch_fp8(p, d_idx, *bufs.args(), None, d_q, d_sf, d_w, recv_q,
+                                                  recv_sf, nsf, 1, recv_src, recv_w, **b)]
+        elif args.fused:
             dispatch = [ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv, recv_src,
                                               recv_w, **b)]
         elif args.hier:
@@ -450,7 +453,8 @@ def main():
                    "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
                    "dispatch": "fp8" if args.fp8 else "bf16",
                    "path": "two-level (group buffer)" if args.hier else "flat",
-                   "layout_dispatch": "one call (ep_layout_dispatch)" if args.fused else "two calls",
+                   "layout_dispatch": ("one call (ep_layout_dispatch_fp8)" if args.fp8 else
+                                       "one call (ep_layout_dispatch)") if args.fused else "two calls",
                    "launch": "hip_graph" if args.graph else "eager"},
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,

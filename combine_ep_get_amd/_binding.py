@@ -27,9 +27,9 @@ EP_MAX_HIDDEN = 1 << 24
 
 # Every function the C header declares, checked by the test-suite.
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
-           "ep_layout_dispatch", "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8", "ep_get_group_layout",
-           "ep_dispatch_hier", "ep_combine_hier", "ep_combine_topk_weights",
-           "ep_read_status", "ep_error_string")
+           "ep_layout_dispatch", "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8",
+           "ep_layout_dispatch_fp8", "ep_get_group_layout", "ep_dispatch_hier", "ep_combine_hier",
+           "ep_combine_topk_weights", "ep_read_status", "ep_error_string")
 
 
 class EpError(RuntimeError):
@@ -91,6 +91,8 @@ def load():
         lib.ep_dispatch_fp8.restype = ctypes.c_int
         lib.ep_dispatch_fp8.argtypes = [P] + [vp] * 6 + [ctypes.c_int64, ctypes.c_int64] + [vp] * 2 + [vp]
         i64 = ctypes.c_int64
+        lib.ep_layout_dispatch_fp8.restype = ctypes.c_int
+        lib.ep_layout_dispatch_fp8.argtypes = [P] + [vp] * 10 + [sz] + [vp] * 5 + [i64, i64] + [vp] * 2 + [vp]
         lib.ep_get_group_layout.restype = ctypes.c_int
         lib.ep_get_group_layout.argtypes = [P, vp, i64, vp, vp]
         lib.ep_dispatch_hier.restype = ctypes.c_int
@@ -219,6 +221,25 @@ def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, 
                                     _ptr(token_slot), _ptr(recv_x_fp8), _ptr(recv_sf),
                                     sf_token_stride, sf_hidden_stride, _ptr(recv_src_token),
                                     _ptr(recv_weight), _stream(stream)), bind)
+
+
+def ep_layout_dispatch_fp8(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                           rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                           cumulative_expert_recv, workspace, workspace_bytes, x_fp8, x_sf,
+                           topk_weights, recv_x_fp8, recv_sf, sf_token_stride, sf_hidden_stride,
+                           recv_src_token=None, recv_weight=None, stream=None, bind=False):
+    """ep_get_layout followed by ep_dispatch_fp8 (one kernel for decode-sized batches)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return _run("ep_layout_dispatch_fp8", (ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
+                                           _ptr(expert_offset), _ptr(rank_row_count),
+                                           _ptr(rank_token_count), _ptr(group_token_count),
+                                           _ptr(is_token_in_rank), _ptr(token_slot),
+                                           _ptr(cumulative_expert_recv), _ptr(workspace),
+                                           workspace_bytes, _ptr(x_fp8), _ptr(x_sf), _ptr(topk_weights),
+                                           _ptr(recv_x_fp8), _ptr(recv_sf), sf_token_stride,
+                                           sf_hidden_stride, _ptr(recv_src_token), _ptr(recv_weight),
+                                           _stream(stream)), bind)
 
 
 def ep_get_group_layout(problem, is_token_in_rank, group_stride_rows, group_slot,

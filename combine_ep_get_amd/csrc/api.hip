@@ -133,6 +133,45 @@ int dispatch_args(const uint16_t *x, const float *topk_weights, const int32_t *t
     return EP_OK;
 }
 
+// Validates the FP8 dispatch call's arguments (H % 128 == 0, scale strides,
+// pointers) and fills c and a.  With no tokens only the sizes are checked.
+int dispatch_fp8_args(const ep_problem *p, const uint8_t *x_fp8, const float *x_sf,
+                      const float *topk_weights, const int32_t *token_slot, uint8_t *recv_x_fp8,
+                      float *recv_sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                      int32_t *recv_src_token, float *recv_weight, epget::CopyParams *c,
+                      epget::DispatchArgs *out) {
+    if (p->hidden % 128 != 0 || sf_token_stride < 1 || sf_hidden_stride < 1)
+        return EP_ERR_INVALID_ARG;
+    const int64_t nsf = p->hidden / 128;
+    const int64_t rows = p->rank_stride_rows * p->num_ranks;
+    // the largest scale index must be addressable
+    if ((rows - 1) > (INT64_MAX - (nsf - 1) * sf_hidden_stride) / sf_token_stride)
+        return EP_ERR_INVALID_ARG;
+    *c = copy_params(p);
+    c->nvec = p->hidden / 16;
+    *out = epget::DispatchArgs{};
+    if (p->num_tokens == 0) return EP_OK;
+    if (!x_fp8 || !x_sf || !token_slot || !recv_x_fp8 || !recv_sf) return EP_ERR_INVALID_ARG;
+    if (!aligned(x_fp8, 16) || !aligned(recv_x_fp8, 16) || !aligned(x_sf, 4) ||
+        !aligned(recv_sf, 4) || !aligned(token_slot, 4) || !aligned(topk_weights, 4) ||
+        !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
+        return EP_ERR_INVALID_ARG;
+    epget::DispatchArgs a = {};
+    a.x = x_fp8;
+    a.w = topk_weights;
+    a.slot = token_slot;
+    a.recv = recv_x_fp8;
+    a.recv_src = recv_src_token;
+    a.recv_w = recv_weight;
+    a.x_sf = x_sf;
+    a.recv_sf = recv_sf;
+    a.sf_ts = sf_token_stride;
+    a.sf_hs = sf_hidden_stride;
+    a.nsf = static_cast<int32_t>(nsf);
+    *out = a;
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,34 +253,33 @@ int ep_dispatch_fp8(const ep_problem *p, const uint8_t *x_fp8, const float *x_sf
                     int32_t *recv_src_token, float *recv_weight, void *stream) {
     int rc = check_problem(p);
     if (rc != EP_OK) return rc;
-    if (p->hidden % 128 != 0 || sf_token_stride < 1 || sf_hidden_stride < 1)
-        return EP_ERR_INVALID_ARG;
-    const int64_t nsf = p->hidden / 128;
-    const int64_t rows = p->rank_stride_rows * p->num_ranks;
-    // the largest scale index must be addressable
-    if ((rows - 1) > (INT64_MAX - (nsf - 1) * sf_hidden_stride) / sf_token_stride)
-        return EP_ERR_INVALID_ARG;
-    if (p->num_tokens == 0) return EP_OK;
-    if (!x_fp8 || !x_sf || !token_slot || !recv_x_fp8 || !recv_sf) return EP_ERR_INVALID_ARG;
-    if (!aligned(x_fp8, 16) || !aligned(recv_x_fp8, 16) || !aligned(x_sf, 4) ||
-        !aligned(recv_sf, 4) || !aligned(token_slot, 4) || !aligned(topk_weights, 4) ||
-        !aligned(recv_src_token, 4) || !aligned(recv_weight, 4))
-        return EP_ERR_INVALID_ARG;
-    epget::CopyParams c = copy_params(p);
-    c.nvec = p->hidden / 16;
-    epget::DispatchArgs a = {};
-    a.x = x_fp8;
-    a.w = topk_weights;
-    a.slot = token_slot;
-    a.recv = recv_x_fp8;
-    a.recv_src = recv_src_token;
-    a.recv_w = recv_weight;
-    a.x_sf = x_sf;
-    a.recv_sf = recv_sf;
-    a.sf_ts = sf_token_stride;
-    a.sf_hs = sf_hidden_stride;
-    a.nsf = static_cast<int32_t>(nsf);
+    epget::CopyParams c;
+    epget::DispatchArgs a;
+    rc = dispatch_fp8_args(p, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, recv_sf,
+                           sf_token_stride, sf_hidden_stride, recv_src_token, recv_weight, &c, &a);
+    if (rc != EP_OK || p->num_tokens == 0) return rc;
     return hip_rc(epget::launch_dispatch(c, a, static_cast<hipStream_t>(stream)));
+}
+
+int ep_layout_dispatch_fp8(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
+                           int32_t *expert_offset, int32_t *rank_row_count, int32_t *rank_token_count,
+                           int32_t *group_token_count, uint8_t *is_token_in_rank, int32_t *token_slot,
+                           int64_t *cumulative_expert_recv, void *workspace, size_t workspace_bytes,
+                           const uint8_t *x_fp8, const float *x_sf, const float *topk_weights,
+                           uint8_t *recv_x_fp8, float *recv_sf, int64_t sf_token_stride,
+                           int64_t sf_hidden_stride, int32_t *recv_src_token, float *recv_weight,
+                           void *stream) {
+    epget::LayoutParams lp;
+    int rc = layout_params(p, topk_idx, expert_count, expert_offset, rank_row_count, rank_token_count,
+                           group_token_count, is_token_in_rank, token_slot, cumulative_expert_recv,
+                           workspace, workspace_bytes, &lp);
+    if (rc != EP_OK) return rc;
+    epget::CopyParams c;
+    epget::DispatchArgs a;
+    rc = dispatch_fp8_args(p, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, recv_sf,
+                           sf_token_stride, sf_hidden_stride, recv_src_token, recv_weight, &c, &a);
+    if (rc != EP_OK) return rc;
+    return hip_rc(epget::launch_layout_dispatch(lp, c, a, static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine(const ep_problem *p, const uint16_t *y, const int32_t *token_slot,

@@ -232,6 +232,22 @@ int ep_dispatch_fp8(const ep_problem *problem, const uint8_t *x_fp8, const float
                     int64_t sf_hidden_stride, int32_t *recv_src_token, float *recv_weight,
                     void *stream);
 
+/* FP8 layout then dispatch in one call: ep_get_layout followed by
+ * ep_dispatch_fp8, with the arguments, outputs, errors and status of both;
+ * one kernel when the batch is one layout chunk, as for ep_layout_dispatch
+ * (decode-sized batches, where [SYM] §9.2's use_fp8_dispatch matters most
+ * for latency). */
+int ep_layout_dispatch_fp8(const ep_problem *problem, const int32_t *topk_idx,
+                           int32_t *expert_count, int32_t *expert_offset,
+                           int32_t *rank_row_count, int32_t *rank_token_count,
+                           int32_t *group_token_count, uint8_t *is_token_in_rank,
+                           int32_t *token_slot, int64_t *cumulative_expert_recv,
+                           void *workspace, size_t workspace_bytes,
+                           const uint8_t *x_fp8, const float *x_sf, const float *topk_weights,
+                           uint8_t *recv_x_fp8, float *recv_sf, int64_t sf_token_stride,
+                           int64_t sf_hidden_stride, int32_t *recv_src_token,
+                           float *recv_weight, void *stream);
+
 /* Two-level (hierarchical) path for G > 1 scale-out groups of R/G ranks:
  * "DeepEP V2 ElasticBuffer 架构深度分析" (hybrid dispatch selected when there
  * is more than one scale-out rank; logical topology block) and [V1] §3.2

@@ -127,3 +127,18 @@ def test_binding_refuses_strided_views():
     view = torch.zeros((8, 16), dtype=torch.int16).t()
     with pytest.raises(ValueError):
         ep.ep_combine(p, view, 1 << 20, None, 1 << 20, stream=0)
+
+
+def test_layout_dispatch_fp8_argument_checks():
+    lib = ep.load()
+    a = 1 << 20
+    need = ep.ep_workspace_bytes(P())
+    lay = [a] * 8
+    p = P(H=7168 + 8)   # not a multiple of 128
+    assert lib.ep_layout_dispatch_fp8(ctypes.byref(p), *lay, None, a, need, a, a, a, a, a, 56, 1,
+                                      a, a, None) == ep.EP_ERR_INVALID_ARG
+    p = P()
+    assert lib.ep_layout_dispatch_fp8(ctypes.byref(p), *lay, None, a, need, a, a, a, a, a, 0, 1,
+                                      a, a, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_layout_dispatch_fp8(ctypes.byref(p), *lay, None, a, need, a + 8, a, a, a, a, 56, 1,
+                                      a, a, None) == ep.EP_ERR_INVALID_ARG

@@ -144,6 +144,40 @@ def test_dispatch_fp8_parity(ep, name, column_major):
     assert_same(g_w.cpu().numpy()[s], rw[s])
 
 
+@pytest.mark.parametrize("name,column_major", [("tiny", False), ("decode128", True), ("decode128", False),
+                                               ("prefill4k", True)])
+def test_layout_dispatch_fp8_parity(ep, name, column_major):
+    """The one-call FP8 layout and dispatch: one kernel for the one-chunk
+    batches, the separate kernels for prefill4k."""
+    inp = ep_inputs.make_inputs(name)
+    wl = inp.wl
+    S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
+    rows = wl.R * S
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, wl.G)
+    q, sf = oracle.quantize_fp8(inp.x)
+    rq, rsf, (ts, hs), rsrc, rw = oracle.dispatch_fp8(q, sf, lay.token_slot, rows, inp.topk_weights,
+                                                     column_major_sf=column_major)
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, 1, S)
+    bufs = ep.alloc_layout(p)
+    g_q = torch.empty((rows, wl.H), dtype=torch.uint8, device="cuda")
+    g_sf = torch.full((rsf.size,), float("nan"), dtype=torch.float32, device="cuda")
+    g_src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ep.ep_layout_dispatch_fp8(p, dev(inp.topk_idx), *bufs.args(), None, dev(q), dev(sf),
+                              dev(inp.topk_weights), g_q, g_sf, ts, hs, g_src, g_w)
+    assert ep.ep_read_status(bufs.workspace) == ep.EP_OK
+    for field in ("expert_count", "expert_offset", "rank_row_count", "rank_token_count",
+                  "is_token_in_rank", "token_slot"):
+        assert_same(getattr(bufs, field).cpu().numpy(), getattr(lay, field), field)
+    s = lay.token_slot.ravel()
+    assert_same(g_q.cpu().numpy()[s], rq[s])
+    nb = wl.H // 128
+    idx = (s[:, None] * ts + np.arange(nb)[None, :] * hs).ravel()
+    assert_same(g_sf.cpu().numpy()[idx], rsf[idx])
+    assert_same(g_src.cpu().numpy()[s], rsrc[s])
+    assert_same(g_w.cpu().numpy()[s], rw[s])
+
+
 def test_fp8_rejects_hidden_not_multiple_of_128(ep):
     p = ep.Problem.make(16, 200, 8, 2, 2, 1, 1, 64)
     with pytest.raises(ep.EpError):
