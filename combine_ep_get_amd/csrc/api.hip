@@ -111,6 +111,8 @@ int layout_params(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
     lp.status = reinterpret_cast<int32_t *>(ws);
     lp.totals = reinterpret_cast<int32_t *>(ws + w.totals_off);
     lp.table = reinterpret_cast<int32_t *>(ws + w.table_off);
+    lp.count_t = reinterpret_cast<int32_t *>(ws + w.count_t_off);
+    lp.excl_t = reinterpret_cast<int32_t *>(ws + w.excl_t_off);
     return EP_OK;
 }
 

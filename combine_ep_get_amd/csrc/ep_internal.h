@@ -16,6 +16,10 @@ constexpr int kChunkEntries = 1024;
 //   [0, 256)                  status word (int32) + padding
 //   [256, 256 + pitch*4)      column totals of the chunk table
 //   [table_off, ...)          chunk table: nchunks rows x pitch int32
+//   [count_t_off, ...)        E x nchunks int32: per-chunk expert counts,
+//                             expert-major (one-call layout and dispatch)
+//   [excl_t_off, ...)         E x nchunks int32: per-chunk counts of the
+//                             lower experts of the same rank, expert-major
 // Columns of the chunk table: E experts | R ranks | G groups | 1 bad-id count.
 struct WsLayout {
     int64_t nchunks;      // >= 1
@@ -24,6 +28,7 @@ struct WsLayout {
     int32_t pitch;        // ncols rounded up to a multiple of 64
     int64_t totals_off;
     int64_t table_off;
+    int64_t count_t_off, excl_t_off;
     int64_t bytes;
 };
 
@@ -53,6 +58,9 @@ struct LayoutParams {
     int32_t *token_slot;
     int64_t *cumulative;  // may be null
     int32_t *status, *totals, *table;
+    // expert-major per-chunk counts and in-rank exclusive prefixes; the count
+    // pass fills them only when non-null (the one-call multi-chunk path)
+    int32_t *count_t, *excl_t;
 };
 
 struct CopyParams {

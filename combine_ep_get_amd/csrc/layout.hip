@@ -34,6 +34,9 @@
 // Layout and dispatch in one launch (one-chunk batches): two workgroups
 // write the layout outputs while every dispatching workgroup derives its own
 // token's slots from LDS histograms of the batch (layout_dispatch_kernel).
+// Up to kMaxCallChunks chunks with A = 1: the count pass, then one launch
+// that does the same from expert-major per-chunk counts
+// (dispatch_chunks_kernel).
 //
 // Every global read a step needs is issued as one batch of independent loads
 // (indices clamped into range, a buffer load's range check where a predicate
@@ -329,9 +332,21 @@ __device__ __forceinline__ void wave_assign_slots(const LayoutParams &p, int64_t
     }
 }
 
-// Multi-chunk pass 1: one workgroup per chunk writes its histogram row.
+template <int NT, int EPT>
+__device__ void block_scan_counts(const LayoutParams &p, const int *counts, int *s_aln,
+                                  int *s_raw, int *s_wsum);
+
+constexpr int kCountEPT = (EP_MAX_EXPERTS + kCountThreads - 1) / kCountThreads;
+
+// Multi-chunk pass 1: one workgroup per chunk writes its histogram row.  For
+// the one-call layout and dispatch (p.count_t set) it also writes, expert-
+// major, the chunk's count of each expert and the chunk's count of the lower
+// experts of the same rank (an exclusive scan of the histogram restarted at
+// each rank's first expert).
+// LDS: s_idx [kChunkEntries] | s_hist [pitch] | s_raw [E+1] | s_aln [E+1].
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(LayoutParams p) {
     extern __shared__ __align__(16) int smem[];
+    __shared__ int s_wsum[2 * kCountThreads / 64];
     int *s_idx = smem;
     int *s_hist = smem + kChunkEntries;
     const int c = blockIdx.x;
@@ -346,6 +361,17 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(LayoutParam
     __syncthreads();
     int32_t *row = p.table + static_cast<int64_t>(c) * p.pitch;
     for (int i = threadIdx.x; i < p.ncols; i += kCountThreads) row[i] = s_hist[i];
+    if (p.count_t) {
+        int *s_raw = s_hist + p.pitch;
+        int *s_aln = s_raw + (p.E + 1);
+        block_scan_counts<kCountThreads, kCountEPT>(p, s_hist, s_aln, s_raw, s_wsum);
+        __syncthreads();
+        for (int e = threadIdx.x; e < p.E; e += kCountThreads) {
+            const int64_t at = static_cast<int64_t>(e) * p.nchunks + c;
+            p.count_t[at] = s_hist[e];
+            p.excl_t[at] = s_raw[e] - s_raw[static_cast<int>(p.div_L(e)) * p.L];
+        }
+    }
 }
 
 // Multi-chunk pass 2: per 64-column tile, rewrite the table in place as
@@ -624,7 +650,7 @@ hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
         layout_one_chunk_kernel<W><<<2, 64 * W, lds, stream>>>(p);
         return hipGetLastError();
     }
-    const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch);
+    const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch + 2 * (p.E + 1));
     layout_count_kernel<<<p.nchunks, kCountThreads, lds_count, stream>>>(p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -730,6 +756,142 @@ __global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutPar
     store_token_rows<VPT>(c, a, t, v0, meta, lane_slot, buf);
 }
 
+// Largest chunk count of the two-launch one-call path: a wave reads one
+// chunk's prefix per lane.
+constexpr int kMaxCallChunks = 64;
+
+// Slots of token t's K entries in chunk c of a multi-chunk batch (A = 1),
+// found by one workgroup of NT threads from the count pass's expert-major
+// arrays instead of a slot walk.  Entry (t, j) with expert e lands at row
+//   sum over chunks of (lower experts of e's rank)     -- expert_offset[e]
+//   + sum over chunks before c of (e)                  -- earlier chunks
+//   + #{entries of chunk c before (t, j) naming e}
+// of its rank's slice, which is the row the walk assigns.  The third term is
+// an LDS histogram of the chunk's entries before token t plus the earlier
+// duplicates of e inside the token.  Returns slot j in lane j of every wave.
+// lds holds E ints.  Contains barriers.
+template <int NT>
+__device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int *s_before,
+                                        int *s_part) {
+    constexpr int kPer = kChunkEntries / NT;
+    constexpr int kWaves = NT / 64;
+    constexpr int kJPerWave = (EP_MAX_TOPK + kWaves - 1) / kWaves;
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
+    const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
+    const int n = (t1 - t0) * p.K;
+    const int32_t *cid = p.topk_idx + static_cast<int64_t>(t0) * p.K;
+    const int lane_id = cid[(t - t0) * p.K + min(lane, p.K - 1)];
+    int ids[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) ids[k] = cid[min(tid + k * NT, n - 1)];
+    // this wave's share of the per-chunk sums: lane l reads chunk l
+    const I32Buffer cnt_t(p.count_t, static_cast<uint32_t>(p.E) * p.nchunks);
+    const I32Buffer exc_t(p.excl_t, static_cast<uint32_t>(p.E) * p.nchunks);
+    int part[kJPerWave];
+#pragma unroll
+    for (int q = 0; q < kJPerWave; ++q) {
+        const int j = w + q * kWaves;
+        const int e = __builtin_amdgcn_readlane(lane_id, min(j, p.K - 1));
+        const bool live = j < p.K && valid_id(e, p.E) && lane < p.nchunks;
+        const uint32_t at = static_cast<uint32_t>(live ? e : 0) * p.nchunks + lane;
+        part[q] = exc_t.load(at, live) + cnt_t.load(at, live && lane < c);
+    }
+    for (int i = tid; i < p.E; i += NT) s_before[i] = 0;
+    __syncthreads();
+    const int before = (t - t0) * p.K;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (tid + k * NT < before && valid_id(ids[k], p.E)) atomicAdd(&s_before[ids[k]], 1);
+#pragma unroll
+    for (int q = 0; q < kJPerWave; ++q) {
+        const int j = w + q * kWaves;
+        if (j < p.K) {
+            const int sum = wave_inclusive_sum(part[q]);
+            if (lane == 63) s_part[j] = sum;
+        }
+    }
+    __syncthreads();
+    const int j = min(lane, p.K - 1);
+    int dup = 0;
+    for (int jj = 0; jj < p.K; ++jj)
+        dup += (jj < j && __builtin_amdgcn_readlane(lane_id, jj) == lane_id) ? 1 : 0;
+    if (!valid_id(lane_id, p.E)) return -1;
+    const int pos = s_part[j] + s_before[lane_id] + dup;
+    return pos < p.S ? static_cast<int>(p.div_L(lane_id)) * p.S + pos : -1;
+}
+
+// The layout outputs of a multi-chunk batch from the count pass's table, by
+// one workgroup of NT threads: totals of every column, per-expert counts and
+// aligned offsets, unique tokens per rank and group, rows per rank and the
+// status.  LDS: s_raw [E+1] | s_aln [E+1].  Contains barriers.
+template <int NT>
+__device__ void finish_layout_from_table(const LayoutParams &p, int *lds) {
+    constexpr int kEPT = (EP_MAX_EXPERTS + NT - 1) / NT;
+    constexpr int kBatch = 16;
+    __shared__ int s_wsum[2 * NT / 64];
+    __shared__ int s_bad, s_over;
+    int *s_raw = lds;
+    int *s_aln = s_raw + (p.E + 1);
+    const int tid = threadIdx.x;
+    const I32Buffer table(p.table, static_cast<uint32_t>(p.nchunks) * p.pitch);
+    if (tid == 0) s_over = 0;
+    // every column has one owner; the last one (bad ids) sets s_bad
+    for (int col = tid; col < p.ncols; col += NT) {
+        int tot = 0;
+        for (int c0 = 0; c0 < p.nchunks; c0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                v[q] = table.load(static_cast<uint32_t>(c0 + q) * p.pitch + col, c0 + q < p.nchunks);
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) tot += v[q];
+        }
+        if (col < p.E) {
+            s_raw[col] = tot;
+            p.expert_count[col] = tot;
+            if (p.cumulative) p.cumulative[col] += tot;
+        } else if (col < p.E + p.R) {
+            p.rank_token_count[col - p.E] = tot;
+        } else if (col < p.E + p.R + p.G) {
+            if (p.group_token_count) p.group_token_count[col - p.E - p.R] = tot;
+        } else {
+            s_bad = tot;
+        }
+    }
+    __syncthreads();
+    block_scan_counts<NT, kEPT>(p, s_raw, s_aln, s_raw, s_wsum);
+    __syncthreads();
+    for (int e = tid; e < p.E; e += NT) p.expert_offset[e] = s_aln[e] - s_aln[static_cast<int>(p.div_L(e)) * p.L];
+    if (finish_ranks<NT>(p, s_aln, s_raw)) atomicOr(&s_over, 1);
+    __syncthreads();
+    if (tid == 0) *p.status = status_code(s_bad > 0, s_over);
+}
+
+// Layout and dispatch of a multi-chunk batch (A = 1, at most kMaxCallChunks
+// chunks) in the launch after the count pass, on a (T, splits + 1) grid:
+// workgroup (0, 0) writes the layout outputs from the table, the rest of row
+// y = 0 has nothing to do, and workgroup (t, y > 0) derives token t's slots,
+// writes them if y == 1, and dispatches column run y - 1 of its row.
+template <int VPT>
+__global__ __launch_bounds__(kCopyThreads) void dispatch_chunks_kernel(LayoutParams p, CopyParams c,
+                                                                       DispatchArgs a) {
+    extern __shared__ __align__(16) int smem[];
+    __shared__ int s_part[EP_MAX_TOPK];
+    if (blockIdx.y == 0) {
+        if (blockIdx.x == 0) finish_layout_from_table<kCopyThreads>(p, smem);
+        return;
+    }
+    const int t = blockIdx.x;
+    const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
+    u32x4 buf[VPT];
+    load_token_row<VPT>(c, a, t, v0, buf);
+    const int32_t lane_slot = token_slots_in_chunk<kCopyThreads>(p, t, t / p.chunk_tokens, smem, s_part);
+    const bool meta = blockIdx.y == 1;
+    if (meta && static_cast<int>(threadIdx.x) < p.K)
+        p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
+    store_token_rows<VPT>(c, a, t, v0, meta, lane_slot, buf);
+}
+
 }  // namespace
 
 WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t R, int32_t G) {
@@ -741,11 +903,16 @@ WsLayout ws_layout(int32_t T, int32_t K, int32_t E, int32_t R, int32_t G) {
     w.pitch = (w.ncols + 63) / 64 * 64;
     w.totals_off = 256;
     w.table_off = w.totals_off + (static_cast<int64_t>(w.pitch) * 4 + 255) / 256 * 256;
-    w.bytes = w.table_off + w.nchunks * w.pitch * 4;
+    const int64_t tr = (static_cast<int64_t>(E) * w.nchunks * 4 + 255) / 256 * 256;
+    w.count_t_off = w.table_off + (w.nchunks * w.pitch * 4 + 255) / 256 * 256;
+    w.excl_t_off = w.count_t_off + tr;
+    w.bytes = w.excl_t_off + tr;
     return w;
 }
 
-hipError_t launch_layout(const LayoutParams &p, hipStream_t stream) {
+hipError_t launch_layout(const LayoutParams &lp, hipStream_t stream) {
+    LayoutParams p = lp;
+    p.count_t = p.excl_t = nullptr;  // only the one-call path reads them
     // Walking waves per chunk: as many as the per-(wave, expert) cursors
     // allow within 64 KB of LDS.
     if (p.E <= 512) return launch_assign<16>(p, stream);
@@ -755,16 +922,43 @@ hipError_t launch_layout(const LayoutParams &p, hipStream_t stream) {
 
 hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, const DispatchArgs &a,
                                   hipStream_t stream) {
-    if (p.nchunks != 1 || p.T == 0) {
-        const hipError_t err = launch_layout(p, stream);
-        if (err != hipSuccess || p.T == 0) return err;
-        return launch_dispatch(c, a, stream);
-    }
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, &splits, &vpt);
     CopyParams cp = c;
     cp.vpt = vpt;
     const dim3 grid(c.T, splits + 1);
+    if (p.T > 0 && p.nchunks > 1 && p.nchunks <= kMaxCallChunks && p.A == 1) {
+        // count pass (with the expert-major arrays), then one launch that
+        // finishes the layout and dispatches, each workgroup deriving its
+        // token's slots
+        const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch + 2 * (p.E + 1));
+        layout_count_kernel<<<p.nchunks, kCountThreads, lds_count, stream>>>(p);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const size_t lds = sizeof(int) * 2 * (p.E + 1);
+        switch (vpt) {
+#define EP_DISPATCH_CHUNKS_CASE(V)                                                  \
+    case V:                                                                         \
+        dispatch_chunks_kernel<V><<<grid, kCopyThreads, lds, stream>>>(p, cp, a);   \
+        break;
+            EP_DISPATCH_CHUNKS_CASE(1)
+            EP_DISPATCH_CHUNKS_CASE(2)
+            EP_DISPATCH_CHUNKS_CASE(3)
+            EP_DISPATCH_CHUNKS_CASE(4)
+            EP_DISPATCH_CHUNKS_CASE(5)
+            EP_DISPATCH_CHUNKS_CASE(6)
+            EP_DISPATCH_CHUNKS_CASE(7)
+            EP_DISPATCH_CHUNKS_CASE(8)
+#undef EP_DISPATCH_CHUNKS_CASE
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    if (p.nchunks != 1 || p.T == 0) {
+        const hipError_t err = launch_layout(p, stream);
+        if (err != hipSuccess || p.T == 0) return err;
+        return launch_dispatch(c, a, stream);
+    }
     // LDS: the larger of the layout workgroup's (ids, histogram, aligned
     // scan) and a dispatch workgroup's (two histograms and a scan)
     const size_t lds = sizeof(int) * std::max<size_t>(kChunkEntries + p.pitch + p.E + 1,

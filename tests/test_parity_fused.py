@@ -1,8 +1,10 @@
 """ep_layout_dispatch (layout and dispatch in one call) vs the CPU oracle.
 
 Decode-sized batches (one layout chunk) run as a single kernel in which each
-dispatching workgroup derives its token's slots itself; larger batches run
-the separate kernels.  Both must give the layout outputs, slots and
+dispatching workgroup derives its token's slots itself; batches of up to 64
+chunks (with expert_alignment 1) run the count pass and then one kernel that
+does the same from the per-chunk counts; other batches run the separate
+kernels.  Both must give the layout outputs, slots and
 dispatched rows of the oracle bit for bit, and must write no receive row
 that no slot names.
 """
@@ -160,3 +162,46 @@ def test_matches_separate_calls_repeatedly(ep):
                       "is_token_in_rank", "token_slot"):
             assert torch.equal(getattr(a, name_), getattr(b, name_)), name_
         assert torch.equal(ra, rb)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_multi_chunk_random_cases(ep, seed):
+    """Two to 64 chunks: -1 entries, duplicates, bad ids, groups, R above a wave."""
+    rng = np.random.default_rng(2000 + seed)
+    R = int(rng.choice([2, 8, 96, 128]))
+    L = int(rng.choice([1, 2, 5, 16]))
+    E = min(R * L, 2048)
+    L = E // R
+    K = int(rng.integers(1, min(E, 9) + 1))
+    chunk_tokens = 1024 // K
+    T = int(rng.integers(chunk_tokens + 1, min(64 * chunk_tokens, 9000) + 1))
+    G = int(rng.choice([g for g in (1, 2, 4) if R % g == 0]))
+    if seed % 2:
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    else:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    idx[rng.random((T, K)) < 0.1] = -1
+    if seed % 3 == 0:
+        idx[rng.integers(0, T, 3), rng.integers(0, K, 3)] = E + 5
+    H = int(rng.choice([8, 64, 520]))
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    run_fused(ep, idx, w, x, E, R, G, cumulative=seed % 4 == 0)
+
+
+@pytest.mark.parametrize("T,K,A,short", [(700, 8, 1, True), (700, 8, 4, False), (65 * 128, 8, 1, False),
+                                         (64 * 128, 8, 1, False), (3000, 3, 1, True)])
+def test_multi_chunk_paths_and_capacity(ep, T, K, A, short):
+    """The two-launch path at its limits (64 chunks, a slice one row short),
+    and the batches that take the separate kernels (A > 1, 65 chunks)."""
+    rng = np.random.default_rng(T + K + A)
+    E, R = 64, 8
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    S = None
+    if short:
+        counts = np.bincount(idx.ravel(), minlength=E)
+        S = tight_stride(counts, E, R, A) - 1
+    x = ep_inputs.bf16_normal(rng, (T, 64))
+    w = rng.random((T, K)).astype(np.float32)
+    ref, _ = run_fused(ep, idx, w, x, E, R, A=A, S=S)
+    assert ref.status == (oracle.CAPACITY if short else oracle.OK)
