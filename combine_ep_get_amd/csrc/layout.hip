@@ -775,7 +775,7 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
                                         int *s_part) {
     constexpr int kPer = kChunkEntries / NT;
     constexpr int kWaves = NT / 64;
-    constexpr int kJPerWave = (EP_MAX_TOPK + kWaves - 1) / kWaves;
+    constexpr int kRound = 4;  // top-k positions per wave and round
     const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
     const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
     const int n = (t1 - t0) * p.K;
@@ -784,30 +784,32 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
     int ids[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) ids[k] = cid[min(tid + k * NT, n - 1)];
-    // this wave's share of the per-chunk sums: lane l reads chunk l
-    const I32Buffer cnt_t(p.count_t, static_cast<uint32_t>(p.E) * p.nchunks);
-    const I32Buffer exc_t(p.excl_t, static_cast<uint32_t>(p.E) * p.nchunks);
-    int part[kJPerWave];
-#pragma unroll
-    for (int q = 0; q < kJPerWave; ++q) {
-        const int j = w + q * kWaves;
-        const int e = __builtin_amdgcn_readlane(lane_id, min(j, p.K - 1));
-        const bool live = j < p.K && valid_id(e, p.E) && lane < p.nchunks;
-        const uint32_t at = static_cast<uint32_t>(live ? e : 0) * p.nchunks + lane;
-        part[q] = exc_t.load(at, live) + cnt_t.load(at, live && lane < c);
-    }
     for (int i = tid; i < p.E; i += NT) s_before[i] = 0;
     __syncthreads();
     const int before = (t - t0) * p.K;
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
         if (tid + k * NT < before && valid_id(ids[k], p.E)) atomicAdd(&s_before[ids[k]], 1);
+    // the per-chunk sums of this wave's top-k positions: lane l reads chunk l
+    const I32Buffer cnt_t(p.count_t, static_cast<uint32_t>(p.E) * p.nchunks);
+    const I32Buffer exc_t(p.excl_t, static_cast<uint32_t>(p.E) * p.nchunks);
+    for (int j0 = w; j0 < p.K; j0 += kWaves * kRound) {
+        int part[kRound];
 #pragma unroll
-    for (int q = 0; q < kJPerWave; ++q) {
-        const int j = w + q * kWaves;
-        if (j < p.K) {
-            const int sum = wave_inclusive_sum(part[q]);
-            if (lane == 63) s_part[j] = sum;
+        for (int q = 0; q < kRound; ++q) {
+            const int j = j0 + q * kWaves;
+            const int e = __builtin_amdgcn_readlane(lane_id, min(j, p.K - 1));
+            const bool live = j < p.K && valid_id(e, p.E) && lane < p.nchunks;
+            const uint32_t at = static_cast<uint32_t>(live ? e : 0) * p.nchunks + lane;
+            part[q] = exc_t.load(at, live) + cnt_t.load(at, live && lane < c);
+        }
+#pragma unroll
+        for (int q = 0; q < kRound; ++q) {
+            const int j = j0 + q * kWaves;
+            if (j < p.K) {
+                const int sum = wave_inclusive_sum(part[q]);
+                if (lane == 63) s_part[j] = sum;
+            }
         }
     }
     __syncthreads();
