@@ -1,10 +1,12 @@
 """Benchmark: MoE layout + dispatch + combine on one MI355X.
 
-One step is one pass of the whole hot path over one batch: ep_get_layout
-(counts, token-to-rank map, offsets, slots), ep_dispatch (row scatter into the
-[R*S, H] receive buffer) and ep_combine (top-k weighted gather-reduce back to
-token order, reading the dispatched buffer as the expert outputs).  Inputs
-are synthetic and seeded (ep_inputs), resident in HBM before timing starts.
+One step is one pass of the whole hot path over one batch: the layout
+(counts, token-to-rank map, offsets, slots) and the dispatch (row scatter into
+the [R*S, H] receive buffer) through the one-call ep_layout_dispatch, or as
+ep_get_layout + ep_dispatch with --two-calls, then ep_combine (top-k weighted
+gather-reduce back to token order, reading the dispatched buffer as the expert
+outputs).  Inputs are synthetic and seeded (ep_inputs), resident in HBM
+before timing starts.
 
 Prints ONE JSON line: tokens/s for the whole step, effective HBM bandwidth,
 the roofline of the dominant kernel (timed live with HIP events on the stream
@@ -12,7 +14,7 @@ the kernels run on) and the CPU oracle's throughput on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload prefill4k]
   python bench.py --copy-probe      # plain device copy: practical HBM ceiling
-  python bench.py --write-traffic FETCH.csv WRITE.csv   # counters -> profiles/traffic.json
+  python bench.py --write-traffic FETCH.csv WRITE.csv   # counters of --two-calls runs -> profiles/traffic.json
 """
 from __future__ import annotations
 
@@ -121,6 +123,8 @@ def write_traffic(workload, fetch_csv, write_csv, copy_bytes=1 << 30):
     bench's own device copy of `copy_bytes` reads and writes exactly that
     many bytes.  Adds the workload to profiles/traffic.json."""
     fetch, write = _counter_kib(fetch_csv), _counter_kib(write_csv)
+    if "dispatch" not in fetch or "layout" not in fetch:
+        raise SystemExit("counter runs must time the calls apart: run the bench with --two-calls")
 
     def copy_kib(fam):
         # the 1 GiB probe copies, not the small host-to-device input copies
@@ -224,15 +228,16 @@ def main():
                     help="capture one step in a HIP graph and time graph replays (no host launch cost)")
     ap.add_argument("--hier", action="store_true",
                     help="two-level path: group layout, dispatch via the group buffer, per-group partial combine")
-    ap.add_argument("--fused", action="store_true",
-                    help="layout and dispatch through ep_layout_dispatch (one kernel for decode-sized batches)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="layout and dispatch as two calls (ep_get_layout + ep_dispatch) instead of the "
+                         "one-call ep_layout_dispatch")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch (e4m3 rows + per-128-channel scales); combine stays bf16")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="build profiles/traffic.json from rocprofv3 --pmc counter CSVs (no GPU needed)")
     args = ap.parse_args()
-    if args.fused and args.hier:
-        ap.error("--fused applies to the flat path only")
+    # the two-level path needs the layout's slots before its group stage
+    fused = not (args.two_calls or args.hier)
 
     # counter records are kept per workload and mode
     traffic_key = args.workload + ("+fp8" if args.fp8 else "") + ("+two-level" if args.hier else "")
@@ -304,16 +309,16 @@ def main():
         gslot = torch.empty((wl.T, G), dtype=torch.int32, device=dev)
         gbuf = torch.empty((G * SG, wl.H), dtype=torch.int16, device=dev)
 
-    def make_calls(st):
+    def make_calls(st, fused):
         """The step's calls on stream st, marshalled once (bound calls), as
-        (layout, dispatch, combine) lists; with --fused the layout list is
+        (layout, dispatch, combine) lists; when fused the layout list is
         empty and the dispatch list holds the one-call layout-and-dispatch."""
         b = dict(stream=st, bind=True)
-        layout = [] if args.fused else [ep.ep_get_layout(p, d_idx, *bufs.args(), **b)]
-        if args.fused and args.fp8:
+        layout = [] if fused else [ep.ep_get_layout(p, d_idx, *bufs.args(), **b)]
+        if fused and args.fp8:
             dispatch = [ep.ep_layout_dispatch_fp8(p, d_idx, *bufs.args(), None, d_q, d_sf, d_w, recv_q,
                                                   recv_sf, nsf, 1, recv_src, recv_w, **b)]
-        elif args.fused:
+        elif fused:
             dispatch = [ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv, recv_src,
                                               recv_w, **b)]
         elif args.hier:
@@ -331,7 +336,7 @@ def main():
             combine = [ep.ep_combine(p, recv, bufs.token_slot, d_w, out, **b)]
         return layout, dispatch, combine
 
-    phases = make_calls(stream)
+    phases = make_calls(stream, fused)
 
     def run(calls):
         for f in calls:
@@ -359,7 +364,7 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         torch.cuda.synchronize()
-        side_calls = make_calls(side)
+        side_calls = make_calls(side, fused)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
             step(calls=side_calls)
@@ -393,6 +398,19 @@ def main():
         "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
         "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
     }
+    two_call_us = None
+    if fused:
+        # the same steps as two calls, so that the layout and the dispatch
+        # are also timed apart
+        split = make_calls(stream, False)
+        for _ in range(3):
+            step(calls=split)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(events[i], calls=split)
+        torch.cuda.synchronize()
+        two_call_us = {k: float(np.mean([e[n].elapsed_time(e[n + 1]) for e in events])) * 1e3
+                       for n, k in enumerate(("layout", "dispatch", "combine"))}
     cold_us = None
     if args.cold:
         # per-phase durations with the last-level cache flushed before each
@@ -421,8 +439,8 @@ def main():
     nbytes = algorithmic_bytes(wl, fp8=args.fp8)
     total_bytes = sum(nbytes.values())
     eff_gbps = total_bytes / (ms_step * 1e-3) / 1e9
-    if args.fused:
-        # layout and dispatch are one launch: report them as one phase
+    if fused:
+        # layout and dispatch are one call: report them as one phase
         fused_ms = phase_ms.pop("layout") + phase_ms.pop("dispatch")
         phase_ms = {"layout_dispatch": fused_ms, **phase_ms}
         nbytes = {"layout_dispatch": nbytes["layout"] + nbytes["dispatch"], "combine": nbytes["combine"]}
@@ -454,13 +472,14 @@ def main():
                    "dispatch": "fp8" if args.fp8 else "bf16",
                    "path": "two-level (group buffer)" if args.hier else "flat",
                    "layout_dispatch": ("one call (ep_layout_dispatch_fp8)" if args.fp8 else
-                                       "one call (ep_layout_dispatch)") if args.fused else "two calls",
+                                       "one call (ep_layout_dispatch)") if fused else "two calls",
                    "launch": "hip_graph" if args.graph else "eager"},
         "effective_hbm_gbps": eff_gbps,
         "frac_of_peak_hbm": eff_gbps / PEAK_HBM_GBPS,
         "us_per_phase": {k: v * 1e3 for k, v in phase_ms.items()},
         "us_per_phase_note": "separate pass of the same steps with an event pair around each call",
         "us_per_phase_cold": cold_us,
+        "us_per_phase_two_calls": two_call_us,
         "us_per_step": ms_step * 1e3,
         "copy_ceiling_gbps": ceiling["gbps_read_plus_write"],
         "us_quantize_fp8": quant_us,
