@@ -15,7 +15,8 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,fused", [("decode128", False), ("prefill4k", False), ("decode128", True)])
+@pytest.mark.parametrize("name,fused", [("decode128", False), ("prefill4k", False), ("decode128", True),
+                                        ("prefill4k", True)])
 def test_graph_replay_matches_eager(name, fused):
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
