@@ -272,6 +272,7 @@ def test_random_shapes(ep, seed):
     (17, 65536, 16, 4, 4),        # 128 KB rows
     (131072, 32, 256, 8, 16),     # 1024 layout chunks: eight rounds of the scan pass
     (5000, 8, 32, 5, 4),          # one 16-byte vector per row
+    (2100, 8200, 64, 4, 8),       # 1025 vectors: a last column run of one vector
 ])
 def test_wide_rows_and_long_batches(ep, T, H, E, K, R):
     rng = np.random.default_rng(T + H)

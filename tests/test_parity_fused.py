@@ -205,3 +205,18 @@ def test_multi_chunk_paths_and_capacity(ep, T, K, A, short):
     w = rng.random((T, K)).astype(np.float32)
     ref, _ = run_fused(ep, idx, w, x, E, R, A=A, S=S)
     assert ref.status == (oracle.CAPACITY if short else oracle.OK)
+
+
+@pytest.mark.parametrize("T,K,H", [(2100, 4, 8200), (2100, 4, 7168), (1100, 8, 2056), (300, 8, 1032),
+                                   (5000, 1, 8)])
+def test_multi_chunk_row_widths(ep, T, K, H):
+    """The two-launch path on rows of 1 to 1025 16-byte vectors (one vector
+    per thread up to several per thread, whole rows and rows split into
+    column runs)."""
+    rng = np.random.default_rng(T * K + H)
+    E, R = 64, 8
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    w = rng.random((T, K)).astype(np.float32)
+    run_fused(ep, idx, w, x, E, R, S=tight_stride(counts, E, R))
