@@ -109,16 +109,72 @@ def load():
     return _lib
 
 
-def _ptr(t):
-    """Device pointer of a tensor, a raw integer address, or NULL for None.
-    The library reads every array densely, so a strided view is refused."""
-    if t is None:
-        return None
-    if isinstance(t, int):
+# Element types the C calls read, by the C type of the argument.
+def _dtypes():
+    import torch
+    return {
+        "int32": (torch.int32,),
+        "int64": (torch.int64,),
+        "float": (torch.float32,),
+        "uint8": (torch.uint8, torch.bool),
+        "bf16": (torch.bfloat16, torch.int16, torch.uint16),
+        "e4m3": (torch.float8_e4m3fn, torch.uint8, torch.int8),
+        "bytes": None,
+    }
+
+
+def _arg(t, what: str, ctype: str, count: int):
+    """Pointer for argument `what` of C element type `ctype`, which the call
+    reads or writes over `count` elements.  None gives NULL; an int is taken
+    as a raw device address, unchecked.  A tensor must be dense, of that
+    element type, hold at least `count` elements (bytes for "bytes") and be
+    on the GPU: the kernels would read past a short array, and a host
+    address in a kernel is a GPU memory fault."""
+    if t is None or isinstance(t, int):
         return t
     if not t.is_contiguous():
-        raise ValueError("libepget takes contiguous arrays; call .contiguous() first")
+        raise ValueError(f"{what}: libepget takes contiguous arrays; call .contiguous() first")
+    allowed = _dtypes()[ctype]
+    if allowed is not None and t.dtype not in allowed:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected one of {allowed}")
+    have = t.numel() * t.element_size() if allowed is None else t.numel()
+    if have < count:
+        raise ValueError(f"{what}: {have} {'bytes' if allowed is None else 'elements'}, "
+                         f"the call uses {count}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: a {t.device.type} tensor; the library takes device memory")
     return t.data_ptr()
+
+
+def _sizes(problem):
+    """T, H, K, E, R, G and the receive rows R * S of a problem."""
+    return (problem.num_tokens, problem.hidden, problem.num_topk, problem.num_experts,
+            problem.num_ranks, problem.num_groups, problem.num_ranks * problem.rank_stride_rows)
+
+
+def _layout_ptrs(problem, topk_idx, expert_count, expert_offset, rank_row_count, rank_token_count,
+                 group_token_count, is_token_in_rank, token_slot, cumulative_expert_recv,
+                 workspace, workspace_bytes):
+    T, _, K, E, R, G, _ = _sizes(problem)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return (_arg(topk_idx, "topk_idx", "int32", T * K), _arg(expert_count, "expert_count", "int32", E),
+            _arg(expert_offset, "expert_offset", "int32", E),
+            _arg(rank_row_count, "rank_row_count", "int32", R),
+            _arg(rank_token_count, "rank_token_count", "int32", R),
+            _arg(group_token_count, "group_token_count", "int32", G),
+            _arg(is_token_in_rank, "is_token_in_rank", "uint8", T * R),
+            _arg(token_slot, "token_slot", "int32", T * K),
+            _arg(cumulative_expert_recv, "cumulative_expert_recv", "int64", E),
+            _arg(workspace, "workspace", "bytes", workspace_bytes), workspace_bytes)
+
+
+def _fp8_rows_ptrs(problem, x_fp8, x_sf, recv_x_fp8, recv_sf, sf_token_stride, sf_hidden_stride):
+    T, H, _, _, _, _, rows = _sizes(problem)
+    nsf = H // 128
+    sf_span = (rows - 1) * sf_token_stride + (nsf - 1) * sf_hidden_stride + 1 if rows and nsf else 0
+    return (_arg(x_fp8, "x_fp8", "e4m3", T * H), _arg(x_sf, "x_sf", "float", T * nsf),
+            _arg(recv_x_fp8, "recv_x_fp8", "e4m3", rows * H), _arg(recv_sf, "recv_sf", "float", sf_span))
 
 
 def _stream(stream):
@@ -174,19 +230,25 @@ def ep_rank_stride_hint(problem: Problem) -> int:
 def ep_get_layout(problem, topk_idx, expert_count, expert_offset, rank_row_count,
                   rank_token_count, group_token_count, is_token_in_rank, token_slot,
                   cumulative_expert_recv, workspace, workspace_bytes=None, stream=None, bind=False):
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    return _run("ep_get_layout", (ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
-                                  _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
-                                  _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
-                                  _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
-                                  _stream(stream)), bind)
+    lay = _layout_ptrs(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                       rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                       cumulative_expert_recv, workspace, workspace_bytes)
+    return _run("ep_get_layout", (ctypes.byref(problem), *lay, _stream(stream)), bind)
+
+
+def _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight):
+    T, H, K, _, _, _, rows = _sizes(problem)
+    return (_arg(x, "x", "bf16", T * H), _arg(topk_weights, "topk_weights", "float", T * K),
+            _arg(recv_x, "recv_x", "bf16", rows * H), _arg(recv_src_token, "recv_src_token", "int32", rows),
+            _arg(recv_weight, "recv_weight", "float", rows))
 
 
 def ep_dispatch(problem, x, topk_weights, token_slot, recv_x, recv_src_token=None,
                 recv_weight=None, stream=None, bind=False):
-    return _run("ep_dispatch", (ctypes.byref(problem), _ptr(x), _ptr(topk_weights), _ptr(token_slot),
-                                _ptr(recv_x), _ptr(recv_src_token), _ptr(recv_weight), _stream(stream)), bind)
+    T, _, K, _, _, _, _ = _sizes(problem)
+    px, pw, prx, psrc, prw = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
+    return _run("ep_dispatch", (ctypes.byref(problem), px, pw, _arg(token_slot, "token_slot", "int32", T * K),
+                                prx, psrc, prw, _stream(stream)), bind)
 
 
 def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_count,
@@ -194,33 +256,40 @@ def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_
                        cumulative_expert_recv, workspace, workspace_bytes, x, topk_weights, recv_x,
                        recv_src_token=None, recv_weight=None, stream=None, bind=False):
     """ep_get_layout followed by ep_dispatch (one kernel for decode-sized batches)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    return _run("ep_layout_dispatch", (ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
-                                       _ptr(expert_offset), _ptr(rank_row_count), _ptr(rank_token_count),
-                                       _ptr(group_token_count), _ptr(is_token_in_rank), _ptr(token_slot),
-                                       _ptr(cumulative_expert_recv), _ptr(workspace), workspace_bytes,
-                                       _ptr(x), _ptr(topk_weights), _ptr(recv_x), _ptr(recv_src_token),
-                                       _ptr(recv_weight), _stream(stream)), bind)
+    lay = _layout_ptrs(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                       rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                       cumulative_expert_recv, workspace, workspace_bytes)
+    rows = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
+    return _run("ep_layout_dispatch", (ctypes.byref(problem), *lay, *rows, _stream(stream)), bind)
 
 
 def ep_combine(problem, y, token_slot, topk_weights, out, stream=None, bind=False):
-    return _run("ep_combine", (ctypes.byref(problem), _ptr(y), _ptr(token_slot), _ptr(topk_weights),
-                               _ptr(out), _stream(stream)), bind)
+    T, H, K, _, _, _, rows = _sizes(problem)
+    return _run("ep_combine", (ctypes.byref(problem), _arg(y, "y", "bf16", rows * H),
+                               _arg(token_slot, "token_slot", "int32", T * K),
+                               _arg(topk_weights, "topk_weights", "float", T * K),
+                               _arg(out, "out", "bf16", T * H), _stream(stream)), bind)
 
 
 def ep_quantize_fp8(problem, x, x_fp8, x_sf, stream=None, bind=False):
-    return _run("ep_quantize_fp8", (ctypes.byref(problem), _ptr(x), _ptr(x_fp8), _ptr(x_sf),
-                                    _stream(stream)), bind)
+    T, H, _, _, _, _, _ = _sizes(problem)
+    return _run("ep_quantize_fp8", (ctypes.byref(problem), _arg(x, "x", "bf16", T * H),
+                                    _arg(x_fp8, "x_fp8", "e4m3", T * H),
+                                    _arg(x_sf, "x_sf", "float", T * (H // 128)), _stream(stream)), bind)
 
 
 def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, recv_sf,
                     sf_token_stride, sf_hidden_stride, recv_src_token=None, recv_weight=None,
                     stream=None, bind=False):
-    return _run("ep_dispatch_fp8", (ctypes.byref(problem), _ptr(x_fp8), _ptr(x_sf), _ptr(topk_weights),
-                                    _ptr(token_slot), _ptr(recv_x_fp8), _ptr(recv_sf),
-                                    sf_token_stride, sf_hidden_stride, _ptr(recv_src_token),
-                                    _ptr(recv_weight), _stream(stream)), bind)
+    T, _, K, _, _, _, rows = _sizes(problem)
+    px, psf, prx, prsf = _fp8_rows_ptrs(problem, x_fp8, x_sf, recv_x_fp8, recv_sf, sf_token_stride,
+                                        sf_hidden_stride)
+    return _run("ep_dispatch_fp8", (ctypes.byref(problem), px, psf,
+                                    _arg(topk_weights, "topk_weights", "float", T * K),
+                                    _arg(token_slot, "token_slot", "int32", T * K), prx, prsf,
+                                    sf_token_stride, sf_hidden_stride,
+                                    _arg(recv_src_token, "recv_src_token", "int32", rows),
+                                    _arg(recv_weight, "recv_weight", "float", rows), _stream(stream)), bind)
 
 
 def ep_layout_dispatch_fp8(problem, topk_idx, expert_count, expert_offset, rank_row_count,
@@ -229,46 +298,61 @@ def ep_layout_dispatch_fp8(problem, topk_idx, expert_count, expert_offset, rank_
                            topk_weights, recv_x_fp8, recv_sf, sf_token_stride, sf_hidden_stride,
                            recv_src_token=None, recv_weight=None, stream=None, bind=False):
     """ep_get_layout followed by ep_dispatch_fp8 (one kernel for decode-sized batches)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    return _run("ep_layout_dispatch_fp8", (ctypes.byref(problem), _ptr(topk_idx), _ptr(expert_count),
-                                           _ptr(expert_offset), _ptr(rank_row_count),
-                                           _ptr(rank_token_count), _ptr(group_token_count),
-                                           _ptr(is_token_in_rank), _ptr(token_slot),
-                                           _ptr(cumulative_expert_recv), _ptr(workspace),
-                                           workspace_bytes, _ptr(x_fp8), _ptr(x_sf), _ptr(topk_weights),
-                                           _ptr(recv_x_fp8), _ptr(recv_sf), sf_token_stride,
-                                           sf_hidden_stride, _ptr(recv_src_token), _ptr(recv_weight),
+    T, _, K, _, _, _, rows = _sizes(problem)
+    lay = _layout_ptrs(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                       rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                       cumulative_expert_recv, workspace, workspace_bytes)
+    px, psf, prx, prsf = _fp8_rows_ptrs(problem, x_fp8, x_sf, recv_x_fp8, recv_sf, sf_token_stride,
+                                        sf_hidden_stride)
+    return _run("ep_layout_dispatch_fp8", (ctypes.byref(problem), *lay, px, psf,
+                                           _arg(topk_weights, "topk_weights", "float", T * K), prx, prsf,
+                                           sf_token_stride, sf_hidden_stride,
+                                           _arg(recv_src_token, "recv_src_token", "int32", rows),
+                                           _arg(recv_weight, "recv_weight", "float", rows),
                                            _stream(stream)), bind)
 
 
 def ep_get_group_layout(problem, is_token_in_rank, group_stride_rows, group_slot,
                         stream=None, bind=False):
-    return _run("ep_get_group_layout", (ctypes.byref(problem), _ptr(is_token_in_rank),
-                                        group_stride_rows, _ptr(group_slot), _stream(stream)), bind)
+    T, _, _, _, R, G, _ = _sizes(problem)
+    return _run("ep_get_group_layout", (ctypes.byref(problem),
+                                        _arg(is_token_in_rank, "is_token_in_rank", "uint8", T * R),
+                                        group_stride_rows, _arg(group_slot, "group_slot", "int32", T * G),
+                                        _stream(stream)), bind)
 
 
 def ep_dispatch_hier(problem, x, topk_weights, token_slot, group_slot, group_stride_rows,
                      group_buf, recv_x, recv_src_token=None, recv_weight=None, stream=None, bind=False):
-    return _run("ep_dispatch_hier", (ctypes.byref(problem), _ptr(x), _ptr(topk_weights),
-                                     _ptr(token_slot), _ptr(group_slot), group_stride_rows,
-                                     _ptr(group_buf), _ptr(recv_x), _ptr(recv_src_token),
-                                     _ptr(recv_weight), _stream(stream)), bind)
+    T, H, K, _, _, G, _ = _sizes(problem)
+    px, pw, prx, psrc, prw = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
+    return _run("ep_dispatch_hier", (ctypes.byref(problem), px, pw,
+                                     _arg(token_slot, "token_slot", "int32", T * K),
+                                     _arg(group_slot, "group_slot", "int32", T * G), group_stride_rows,
+                                     _arg(group_buf, "group_buf", "bf16", G * group_stride_rows * H),
+                                     prx, psrc, prw, _stream(stream)), bind)
 
 
 def ep_combine_hier(problem, y, token_slot, topk_weights, group_slot, group_stride_rows,
                     group_buf, out, stream=None, bind=False):
-    return _run("ep_combine_hier", (ctypes.byref(problem), _ptr(y), _ptr(token_slot),
-                                    _ptr(topk_weights), _ptr(group_slot), group_stride_rows,
-                                    _ptr(group_buf), _ptr(out), _stream(stream)), bind)
+    T, H, K, _, _, G, rows = _sizes(problem)
+    return _run("ep_combine_hier", (ctypes.byref(problem), _arg(y, "y", "bf16", rows * H),
+                                    _arg(token_slot, "token_slot", "int32", T * K),
+                                    _arg(topk_weights, "topk_weights", "float", T * K),
+                                    _arg(group_slot, "group_slot", "int32", T * G), group_stride_rows,
+                                    _arg(group_buf, "group_buf", "bf16", G * group_stride_rows * H),
+                                    _arg(out, "out", "bf16", T * H), _stream(stream)), bind)
 
 
 def ep_combine_topk_weights(problem, recv_weight, token_slot, combined_topk_weights,
                             stream=None, bind=False):
-    return _run("ep_combine_topk_weights", (ctypes.byref(problem), _ptr(recv_weight), _ptr(token_slot),
-                                            _ptr(combined_topk_weights), _stream(stream)), bind)
+    T, _, K, _, _, _, rows = _sizes(problem)
+    return _run("ep_combine_topk_weights", (ctypes.byref(problem),
+                                            _arg(recv_weight, "recv_weight", "float", rows),
+                                            _arg(token_slot, "token_slot", "int32", T * K),
+                                            _arg(combined_topk_weights, "combined_topk_weights", "float",
+                                                 T * K), _stream(stream)), bind)
 
 
 def ep_read_status(workspace, stream=None) -> int:
     """Synchronises the stream and returns the layout's device status code."""
-    return load().ep_read_status(_ptr(workspace), _stream(stream))
+    return load().ep_read_status(_arg(workspace, "workspace", "bytes", 4), _stream(stream))

@@ -125,8 +125,38 @@ def test_binding_refuses_strided_views():
     import torch
     p = P()
     view = torch.zeros((8, 16), dtype=torch.int16).t()
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="contiguous"):
         ep.ep_combine(p, view, 1 << 20, None, 1 << 20, stream=0)
+
+
+def test_binding_checks_types_sizes_and_device():
+    """The binding refuses, before any call, arrays of the wrong element type,
+    arrays shorter than the problem needs and host tensors (a kernel would
+    read past the first and fault on the others)."""
+    import torch
+    T, H, K, E, R = 4, 64, 2, 8, 2
+    p = ep.Problem.make(T, H, E, K, R, 1, 1, 8)
+    rows = R * 8
+    a = 1 << 20
+    slot = torch.zeros((T, K), dtype=torch.int32)
+    with pytest.raises(ValueError, match="token_slot: dtype"):
+        ep.ep_combine(p, a, slot.long(), None, a, stream=0)
+    with pytest.raises(ValueError, match="topk_weights: dtype"):
+        ep.ep_combine(p, a, a, torch.zeros((T, K), dtype=torch.float64), a, stream=0)
+    with pytest.raises(ValueError, match="y: 1023 elements, the call uses 1024"):
+        ep.ep_combine(p, torch.zeros(rows * H - 1, dtype=torch.int16), a, None, a, stream=0)
+    with pytest.raises(ValueError, match="out: dtype"):
+        ep.ep_combine(p, a, a, None, torch.zeros((T, H), dtype=torch.float32), stream=0)
+    with pytest.raises(ValueError, match="token_slot: a cpu tensor"):
+        ep.ep_combine(p, a, slot, None, a, stream=0)
+    with pytest.raises(ValueError, match="recv_src_token: 15 elements"):
+        ep.ep_dispatch(p, a, None, a, a, torch.zeros(rows - 1, dtype=torch.int32), stream=0)
+    with pytest.raises(ValueError, match="workspace: 100 bytes, the call uses 4096"):
+        ep.ep_get_layout(p, a, a, a, a, a, None, a, a, None, torch.zeros(100, dtype=torch.uint8), 4096,
+                         stream=0)
+    with pytest.raises(ValueError, match="recv_sf: 10 elements"):
+        ep.ep_dispatch_fp8(ep.Problem.make(T, 128, E, K, R, 1, 1, 8), a, a, None, a, a,
+                           torch.zeros(10, dtype=torch.float32), 1, 1, stream=0)
 
 
 def test_layout_dispatch_fp8_argument_checks():
