@@ -15,7 +15,9 @@
  * Conventions for every entry point:
  *   - All pointers named "device" point to device memory the caller owns
  *     (allocated e.g. by PyTorch); the library allocates and frees nothing
- *     and keeps no state between calls.
+ *     and keeps no state between calls.  Every array must hold at least the
+ *     elements its stated shape implies: the kernels index it by the
+ *     problem's sizes and cannot see its length.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  The hot
  *     calls (ep_get_layout, ep_dispatch, ep_combine) only enqueue kernels:
  *     they never synchronise, so their results are ready when the stream
