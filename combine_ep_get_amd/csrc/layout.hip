@@ -756,9 +756,11 @@ __global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutPar
     store_token_rows<VPT>(c, a, t, v0, meta, lane_slot, buf);
 }
 
-// Largest chunk count of the two-launch one-call path: a wave reads one
-// chunk's prefix per lane.
-constexpr int kMaxCallChunks = 64;
+// Largest chunk count of the two-launch one-call path: a wave reads the
+// per-chunk counts with one lane per chunk, in CR <= kMaxChunkRounds rounds
+// of 64 chunks.
+constexpr int kMaxChunkRounds = 2;
+constexpr int kMaxCallChunks = 64 * kMaxChunkRounds;
 
 // Slots of token t's K entries in chunk c of a multi-chunk batch (A = 1),
 // found by one workgroup of NT threads from the count pass's expert-major
@@ -768,9 +770,10 @@ constexpr int kMaxCallChunks = 64;
 //   + #{entries of chunk c before (t, j) naming e}
 // of its rank's slice, which is the row the walk assigns.  The third term is
 // an LDS histogram of the chunk's entries before token t plus the earlier
-// duplicates of e inside the token.  Returns slot j in lane j of every wave.
+// duplicates of e inside the token.  The per-chunk sums take CR rounds of
+// 64 chunks (one lane per chunk).  Returns slot j in lane j of every wave.
 // lds holds E ints.  Contains barriers.
-template <int NT>
+template <int NT, int CR>
 __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int *s_before,
                                         int *s_part) {
     constexpr int kPer = kChunkEntries / NT;
@@ -790,7 +793,8 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
         if (tid + k * NT < before && valid_id(ids[k], p.E)) atomicAdd(&s_before[ids[k]], 1);
-    // the per-chunk sums of this wave's top-k positions: lane l reads chunk l
+    // the per-chunk sums of this wave's top-k positions: lane l reads chunks
+    // l, l + 64, ...
     const I32Buffer cnt_t(p.count_t, static_cast<uint32_t>(p.E) * p.nchunks);
     const I32Buffer exc_t(p.excl_t, static_cast<uint32_t>(p.E) * p.nchunks);
     for (int j0 = w; j0 < p.K; j0 += kWaves * kRound) {
@@ -799,9 +803,15 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
         for (int q = 0; q < kRound; ++q) {
             const int j = j0 + q * kWaves;
             const int e = __builtin_amdgcn_readlane(lane_id, min(j, p.K - 1));
-            const bool live = j < p.K && valid_id(e, p.E) && lane < p.nchunks;
-            const uint32_t at = static_cast<uint32_t>(live ? e : 0) * p.nchunks + lane;
-            part[q] = exc_t.load(at, live) + cnt_t.load(at, live && lane < c);
+            const bool live = j < p.K && valid_id(e, p.E);
+            const uint32_t row = static_cast<uint32_t>(live ? e : 0) * p.nchunks;
+            part[q] = 0;
+#pragma unroll
+            for (int r = 0; r < CR; ++r) {
+                const int cc = lane + 64 * r;
+                const bool ok = live && cc < p.nchunks;
+                part[q] += exc_t.load(row + cc, ok) + cnt_t.load(row + cc, ok && cc < c);
+            }
         }
 #pragma unroll
         for (int q = 0; q < kRound; ++q) {
@@ -874,7 +884,7 @@ __device__ void finish_layout_from_table(const LayoutParams &p, int *lds) {
 // workgroup (0, 0) writes the layout outputs from the table, the rest of row
 // y = 0 has nothing to do, and workgroup (t, y > 0) derives token t's slots,
 // writes them if y == 1, and dispatches column run y - 1 of its row.
-template <int VPT>
+template <int VPT, int CR>
 __global__ __launch_bounds__(kCopyThreads) void dispatch_chunks_kernel(LayoutParams p, CopyParams c,
                                                                        DispatchArgs a) {
     extern __shared__ __align__(16) int smem[];
@@ -887,7 +897,7 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_chunks_kernel(LayoutPar
     const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
     load_token_row<VPT>(c, a, t, v0, buf);
-    const int32_t lane_slot = token_slots_in_chunk<kCopyThreads>(p, t, t / p.chunk_tokens, smem, s_part);
+    const int32_t lane_slot = token_slots_in_chunk<kCopyThreads, CR>(p, t, t / p.chunk_tokens, smem, s_part);
     const bool meta = blockIdx.y == 1;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
@@ -938,10 +948,15 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         const size_t lds = sizeof(int) * 2 * (p.E + 1);
+        static_assert(kMaxChunkRounds == 2, "the launch instantiates one and two rounds");
+        const bool two_rounds = p.nchunks > 64;
         switch (vpt) {
-#define EP_DISPATCH_CHUNKS_CASE(V)                                                  \
-    case V:                                                                         \
-        dispatch_chunks_kernel<V><<<grid, kCopyThreads, lds, stream>>>(p, cp, a);   \
+#define EP_DISPATCH_CHUNKS_CASE(V)                                                         \
+    case V:                                                                                \
+        if (two_rounds)                                                                    \
+            dispatch_chunks_kernel<V, 2><<<grid, kCopyThreads, lds, stream>>>(p, cp, a);   \
+        else                                                                               \
+            dispatch_chunks_kernel<V, 1><<<grid, kCopyThreads, lds, stream>>>(p, cp, a);   \
         break;
             EP_DISPATCH_CHUNKS_CASE(1)
             EP_DISPATCH_CHUNKS_CASE(2)
