@@ -785,9 +785,9 @@ constexpr int kMaxCallChunks = 64 * kMaxChunkRounds;
 // duplicates of e inside the token.  The per-chunk sums take CR rounds of
 // 64 chunks (one lane per chunk).  Returns slot j in lane j of every wave.
 // lds holds E ints.  Contains barriers.
-template <int NT, int CR>
-__device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int *s_before,
-                                        int *s_part) {
+template <int NT, int CR, bool kEarlySums, class IssueRow>
+__device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int *s_before, int *s_part,
+                                        IssueRow issue_row) {
     constexpr int kPer = kChunkEntries / NT;
     constexpr int kWaves = NT / 64;
     constexpr int kRound = 4;  // top-k positions per wave and round
@@ -795,22 +795,19 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
     const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
     const int n = (t1 - t0) * p.K;
     const int32_t *cid = p.topk_idx + static_cast<int64_t>(t0) * p.K;
+    // the caller's loads of the token's row go first, or right behind the
+    // token's ids when the sums are loaded early (which need those ids)
+    if constexpr (!kEarlySums) issue_row();
     const int lane_id = cid[(t - t0) * p.K + min(lane, p.K - 1)];
-    int ids[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) ids[k] = cid[min(tid + k * NT, n - 1)];
-    for (int i = tid; i < p.E; i += NT) s_before[i] = 0;
-    __syncthreads();
-    const int before = (t - t0) * p.K;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-        if (tid + k * NT < before && valid_id(ids[k], p.E)) atomicAdd(&s_before[ids[k]], 1);
-    // the per-chunk sums of this wave's top-k positions: lane l reads chunks
-    // l, l + 64, ...
+    if constexpr (kEarlySums) {
+        issue_row();
+        __builtin_amdgcn_sched_barrier(0);  // keep the row loads ahead of the sums
+    }
+    // the per-chunk sums of top-k positions j0 + q * kWaves: lane l reads
+    // chunks l, l + 64, ...
     const I32Buffer cnt_t(p.count_t, static_cast<uint32_t>(p.E) * p.nchunks);
     const I32Buffer exc_t(p.excl_t, static_cast<uint32_t>(p.E) * p.nchunks);
-    for (int j0 = w; j0 < p.K; j0 += kWaves * kRound) {
-        int part[kRound];
+    auto load_sums = [&](int j0, int (&part)[kRound]) {
 #pragma unroll
         for (int q = 0; q < kRound; ++q) {
             const int j = j0 + q * kWaves;
@@ -825,6 +822,8 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
                 part[q] += exc_t.load(row + cc, ok) + cnt_t.load(row + cc, ok && cc < c);
             }
         }
+    };
+    auto reduce_sums = [&](int j0, const int (&part)[kRound]) {
 #pragma unroll
         for (int q = 0; q < kRound; ++q) {
             const int j = j0 + q * kWaves;
@@ -833,6 +832,29 @@ __device__ int32_t token_slots_in_chunk(const LayoutParams &p, int t, int c, int
                 if (lane == 63) s_part[j] = sum;
             }
         }
+    };
+    // with kEarlySums the first round's sums are loaded as soon as the
+    // token's ids are in, so that they travel with the row and the chunk's
+    // ids (more registers live at once); otherwise after the histogram
+    int part[kRound];
+    if constexpr (kEarlySums) load_sums(w, part);
+    int ids[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) ids[k] = cid[min(tid + k * NT, n - 1)];
+    for (int i = tid; i < p.E; i += NT) s_before[i] = 0;
+    __syncthreads();
+    const int before = (t - t0) * p.K;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (tid + k * NT < before && valid_id(ids[k], p.E)) atomicAdd(&s_before[ids[k]], 1);
+    int j0 = w;
+    if constexpr (kEarlySums) {
+        reduce_sums(j0, part);
+        j0 += kWaves * kRound;
+    }
+    for (; j0 < p.K; j0 += kWaves * kRound) {
+        load_sums(j0, part);
+        reduce_sums(j0, part);
     }
     __syncthreads();
     const int j = min(lane, p.K - 1);
@@ -908,8 +930,12 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_chunks_kernel(LayoutPar
     const int t = blockIdx.x;
     const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
-    load_token_row<VPT>(c, a, t, v0, buf);
-    const int32_t lane_slot = token_slots_in_chunk<kCopyThreads, CR>(p, t, t / p.chunk_tokens, smem, s_part);
+    // early sums pay when the kernel still fits 64 VGPRs (16 workgroups per
+    // CU) or when a batch of more than 64 chunks needs several rounds of
+    // resident workgroups anyway
+    constexpr bool kEarlySums = CR > 1 || VPT <= 4;
+    const int32_t lane_slot = token_slots_in_chunk<kCopyThreads, CR, kEarlySums>(
+        p, t, t / p.chunk_tokens, smem, s_part, [&] { load_token_row<VPT>(c, a, t, v0, buf); });
     const bool meta = blockIdx.y == 1;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
