@@ -34,8 +34,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     return v;
 }
 
-// Dispatch of one token by one workgroup of kCopyThreads threads, which owns
-// the 16-byte column vectors v0 + v * kCopyThreads (v < VPT) of the row.
+// Dispatch of one token by one workgroup of NT threads, which owns the
+// 16-byte column vectors v0 + v * NT (v < VPT) of the row.
 // Rows are moved as 16-byte vectors whatever their element type (bf16, or
 // e4m3 codes with per-row scale factors).
 //
@@ -43,12 +43,12 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 // (the column is clamped into the row) so they issue back to back; x is read
 // once, so they carry the non-temporal hint (measured about 1 µs faster on a
 // 4096-token step).
-template <int VPT>
+template <int VPT, int NT = kCopyThreads>
 __device__ __forceinline__ void load_token_row(const CopyParams &c, const DispatchArgs &a, int t, int v0,
                                                u32x4 (&buf)[VPT]) {
     const u32x4 *src = static_cast<const u32x4 *>(a.x) + static_cast<int64_t>(t) * c.nvec;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) buf[v] = __builtin_nontemporal_load(src + min(v0 + v * kCopyThreads, c.nvec - 1));
+    for (int v = 0; v < VPT; ++v) buf[v] = __builtin_nontemporal_load(src + min(v0 + v * NT, c.nvec - 1));
 }
 
 // Slot j of the token, held by lane j of every wave (j < K <= 32): a
@@ -69,7 +69,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // store_token_rows: the vectors to the K destination rows (a row outside
 // [0, num_rows) is skipped); with `meta`, also each received row's source
 // token and weight and its scale factors.  lane_slot as for slot_of.
-template <int VPT>
+template <int VPT, int NT = kCopyThreads>
 __device__ __forceinline__ void store_token_rows(const CopyParams &c, const DispatchArgs &a, int t, int v0,
                                                  bool meta, int32_t lane_slot, const u32x4 (&buf)[VPT]) {
     if (meta) {
@@ -82,7 +82,7 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
         }
         // per-row scale factors, one thread per block of channels
         if (a.x_sf) {
-            for (int b = threadIdx.x; b < a.nsf; b += kCopyThreads) {
+            for (int b = threadIdx.x; b < a.nsf; b += NT) {
                 const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
                 for (int j = 0; j < c.K; ++j) {
                     const int32_t s = slot_of(lane_slot, j);
@@ -98,7 +98,7 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
         u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const int col = v0 + v * kCopyThreads;
+            const int col = v0 + v * NT;
             if (col < c.nvec) dst[col] = buf[v];
         }
         if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -94,6 +94,7 @@ struct HierParams {
 };
 
 constexpr int kCopyThreads = 128;      // dispatch workgroup size
+constexpr int kFusedThreads = 256;     // workgroup of the one-chunk layout + dispatch kernel
 constexpr int kMaxVpt = 8;            // dispatch vectors per thread
 constexpr int kCombineMaxThreads = 1024;
 
@@ -117,9 +118,10 @@ hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, cons
 hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, const int32_t *slot,
                                   float *combined_w, hipStream_t stream);
 
-// Grid shape for the row kernels: (tokens, column splits) and vectors per
-// thread, chosen so that small batches still spread over all CUs.
-void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt);
+// Grid shape for the row kernels with workgroups of `threads`: (tokens,
+// column splits) and vectors per thread, chosen so that small batches still
+// spread over all CUs.
+void copy_grid(int32_t T, int32_t nvec, int32_t threads, int32_t *splits, int32_t *vpt);
 // Grid of the combine: (tokens, row pieces) and threads per workgroup (one
 // 16-byte column vector per thread).
 void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads);

@@ -742,13 +742,13 @@ __device__ __forceinline__ int32_t token_slots_one_chunk(const LayoutParams &p, 
 // gives them, which the combine's grid shares: rows a small batch leaves in
 // an XCD's L2 are read back there.
 template <int VPT>
-__global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutParams p, CopyParams c,
+__global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutParams p, CopyParams c,
                                                                        DispatchArgs a) {
     extern __shared__ __align__(16) int smem[];
-    __shared__ int s_wsum[2 * kCopyThreads / 64];
+    __shared__ int s_wsum[2 * kFusedThreads / 64];
     if (blockIdx.y == 0) {
         // the layout, split over workgroups (0, 0) and (1, 0) when there are two
-        constexpr int W = kCopyThreads / 64;
+        constexpr int W = kFusedThreads / 64;
         if (gridDim.x == 1)
             assign_chunk<W, kFusedChunk, false, kLayoutAll>(p, 0);
         else if (blockIdx.x == 0)
@@ -758,14 +758,14 @@ __global__ __launch_bounds__(kCopyThreads) void layout_dispatch_kernel(LayoutPar
         return;
     }
     const int t = blockIdx.x;
-    const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
+    const int v0 = (blockIdx.y - 1) * (kFusedThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
-    load_token_row<VPT>(c, a, t, v0, buf);
-    const int32_t lane_slot = token_slots_one_chunk<kCopyThreads>(p, t, smem, s_wsum);
+    load_token_row<VPT, kFusedThreads>(c, a, t, v0, buf);
+    const int32_t lane_slot = token_slots_one_chunk<kFusedThreads>(p, t, smem, s_wsum);
     const bool meta = blockIdx.y == 1;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
-    store_token_rows<VPT>(c, a, t, v0, meta, lane_slot, buf);
+    store_token_rows<VPT, kFusedThreads>(c, a, t, v0, meta, lane_slot, buf);
 }
 
 // Largest chunk count of the two-launch one-call path: a wave reads the
@@ -972,8 +972,11 @@ hipError_t launch_layout(const LayoutParams &lp, hipStream_t stream) {
 
 hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, const DispatchArgs &a,
                                   hipStream_t stream) {
+    // the one-chunk kernel has larger workgroups: its slot derivation is on
+    // the critical path, and 256 threads share it faster than 128
+    const bool one_chunk = p.T > 0 && p.nchunks == 1;
     int32_t splits, vpt;
-    copy_grid(c.T, c.nvec, &splits, &vpt);
+    copy_grid(c.T, c.nvec, one_chunk ? kFusedThreads : kCopyThreads, &splits, &vpt);
     CopyParams cp = c;
     cp.vpt = vpt;
     const dim3 grid(c.T, splits + 1);
@@ -1021,7 +1024,7 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
     switch (vpt) {
 #define EP_LAYOUT_DISPATCH_CASE(V)                                                 \
     case V:                                                                        \
-        layout_dispatch_kernel<V><<<grid, kCopyThreads, lds, stream>>>(p, cp, a);  \
+        layout_dispatch_kernel<V><<<grid, kFusedThreads, lds, stream>>>(p, cp, a); \
         break;
         EP_LAYOUT_DISPATCH_CASE(1)
         EP_LAYOUT_DISPATCH_CASE(2)

@@ -330,17 +330,17 @@ __global__ __launch_bounds__(256) void combine_weights_kernel(CopyParams c, cons
 
 }  // namespace
 
-void copy_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *vpt) {
+void copy_grid(int32_t T, int32_t nvec, int32_t threads, int32_t *splits, int32_t *vpt) {
     // Aim for at least ~2048 workgroups (8 per CU) so that decode-sized
     // batches still cover the chip; large batches get one workgroup per token
     // and several vectors per thread.
     const int64_t want_blocks = 2048;
     int64_t need = T >= want_blocks ? 1 : (want_blocks + (T > 0 ? T : 1) - 1) / (T > 0 ? T : 1);
-    int64_t v = (nvec + kCopyThreads * need - 1) / (kCopyThreads * need);
+    int64_t v = (nvec + threads * need - 1) / (threads * need);
     if (v < 1) v = 1;
     if (v > kMaxVpt) v = kMaxVpt;
     *vpt = static_cast<int32_t>(v);
-    *splits = static_cast<int32_t>((nvec + kCopyThreads * v - 1) / (kCopyThreads * v));
+    *splits = static_cast<int32_t>((nvec + threads * v - 1) / (threads * v));
 }
 
 void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
@@ -360,7 +360,7 @@ void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
 
 hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream) {
     int32_t splits, vpt;
-    copy_grid(c.T, c.nvec, &splits, &vpt);
+    copy_grid(c.T, c.nvec, kCopyThreads, &splits, &vpt);
     CopyParams p = c;
     p.vpt = vpt;
     dim3 grid(c.T, splits);
@@ -425,7 +425,7 @@ hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const 
 hipError_t launch_expand(const CopyParams &c, const HierParams &h, const DispatchArgs &a,
                          const int32_t *group_slot, const uint16_t *group_buf, hipStream_t stream) {
     int32_t splits, vpt;
-    copy_grid(c.T, c.nvec, &splits, &vpt);
+    copy_grid(c.T, c.nvec, kCopyThreads, &splits, &vpt);
     CopyParams p = c;
     p.vpt = vpt;
     dim3 grid(c.T, splits);
