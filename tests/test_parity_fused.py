@@ -64,12 +64,19 @@ def run_fused(ep, idx, w, x, E, R, G=1, A=1, S=None, cumulative=False, weights=T
     return ref, bufs
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode128", "prefill4k"])
+@pytest.mark.parametrize("name", ["tiny", "decode128", "prefill4k", "zipf8k", "large16k"])
 def test_workloads(ep, name):
+    """Every workload through the call the benchmark times: one chunk
+    (tiny, decode128), 32 and 64 chunks with the per-chunk sums loaded late
+    and early (prefill4k, zipf8k), 128 chunks in two rounds (large16k).  The
+    default stride too where its receive buffer stays small."""
     inp = ep_inputs.make_inputs(name)
     wl = inp.wl
     counts = np.bincount(inp.topk_idx.ravel(), minlength=wl.E)
-    for S in (tight_stride(counts, wl.E, wl.R), None):
+    strides = [tight_stride(counts, wl.E, wl.R)]
+    if name in ("tiny", "decode128", "prefill4k"):
+        strides.append(None)
+    for S in strides:
         run_fused(ep, inp.topk_idx, inp.topk_weights, inp.x, wl.E, wl.R, wl.G, wl.A, S)
 
 
