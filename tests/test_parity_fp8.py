@@ -148,7 +148,7 @@ def test_dispatch_fp8_parity(ep, name, column_major):
                                                ("prefill4k", True)])
 def test_layout_dispatch_fp8_parity(ep, name, column_major):
     """The one-call FP8 layout and dispatch: one kernel for the one-chunk
-    batches, the separate kernels for prefill4k."""
+    batches, the count pass and one kernel for prefill4k (32 chunks)."""
     inp = ep_inputs.make_inputs(name)
     wl = inp.wl
     S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
