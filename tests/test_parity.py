@@ -281,6 +281,14 @@ def test_wide_rows_and_long_batches(ep, T, H, E, K, R):
     _case(ep, idx, E, R, H=H, seed=T)
 
 
+def test_largest_hidden_size(ep):
+    """Rows of EP_MAX_HIDDEN channels (32 MiB): thousands of column pieces
+    per token in every row kernel."""
+    idx = np.array([[0, 3], [2, 1], [3, 0]], np.int32)
+    print(f"[parity] H={ep.EP_MAX_HIDDEN}", flush=True)
+    _case(ep, idx, E=4, R=2, H=ep.EP_MAX_HIDDEN, seed=5)
+
+
 def test_large_expert_count_and_rank_count(ep):
     rng = np.random.default_rng(8)
     E, R, K, T = 2048, 1024, 32, 1500

@@ -231,3 +231,12 @@ def test_multi_chunk_row_widths(ep, T, K, H):
     x = ep_inputs.bf16_normal(rng, (T, H))
     w = rng.random((T, K)).astype(np.float32)
     run_fused(ep, idx, w, x, E, R, S=tight_stride(counts, E, R))
+
+
+def test_largest_hidden_size(ep):
+    """The one-chunk kernel on rows of EP_MAX_HIDDEN channels (32 MiB)."""
+    rng = np.random.default_rng(6)
+    idx = np.array([[0, 3], [2, 1], [3, 0]], np.int32)
+    x = ep_inputs.bf16_normal(rng, (3, ep.EP_MAX_HIDDEN))
+    w = rng.random((3, 2)).astype(np.float32)
+    run_fused(ep, idx, w, x, 4, 2)
