@@ -15,22 +15,16 @@ __device__ __forceinline__ bool slot_ok(int32_t s, int64_t num_rows) {
 
 // Inclusive prefix sum across the 64 lanes of a wave with DPP moves: shifts
 // by 1, 2, 4, 8 inside each row of 16 lanes, then the broadcasts of lane 15
-// and lane 31 into the following rows.
+// into rows 1 and 3 and of lane 31 into rows 2 and 3.  Lanes whose source is
+// outside the row read 0 (bound control) and the broadcasts write 0 to the
+// rows their mask leaves out, so every step is one add with a DPP operand.
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
-    const int lane = __lane_id();
-    const int row_lane = lane & 15;
-    int t = __builtin_amdgcn_mov_dpp(v, 0x111, 0xF, 0xF, false);  // row_shr:1
-    v += row_lane >= 1 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x112, 0xF, 0xF, false);  // row_shr:2
-    v += row_lane >= 2 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    v += row_lane >= 4 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x118, 0xF, 0xF, false);  // row_shr:8
-    v += row_lane >= 8 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x142, 0xF, 0xF, false);  // row_bcast:15
-    v += (lane & 31) >= 16 ? t : 0;
-    t = __builtin_amdgcn_mov_dpp(v, 0x143, 0xF, 0xF, false);  // row_bcast:31
-    v += lane >= 32 ? t : 0;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
     return v;
 }
 
