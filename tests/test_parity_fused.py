@@ -240,3 +240,15 @@ def test_largest_hidden_size(ep):
     x = ep_inputs.bf16_normal(rng, (3, ep.EP_MAX_HIDDEN))
     w = rng.random((3, 2)).astype(np.float32)
     run_fused(ep, idx, w, x, 4, 2)
+
+
+@pytest.mark.parametrize("T,K,E,R,G", [(3000, 32, 2048, 8, 2), (1500, 32, 64, 64, 4), (2000, 17, 512, 128, 4)])
+def test_multi_chunk_wide_top_k(ep, T, K, E, R, G):
+    """Top-k up to 32 across many chunks: several rounds of positions per wave,
+    256 experts per rank, one expert per rank, R above a wave."""
+    rng = np.random.default_rng(T + K + E)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    x = ep_inputs.bf16_normal(rng, (T, 64))
+    w = rng.random((T, K)).astype(np.float32)
+    run_fused(ep, idx, w, x, E, R, G, S=tight_stride(counts, E, R), cumulative=True)
