@@ -24,17 +24,17 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// One workgroup per (token, run of columns): each thread loads its VPT
-// vectors of x[t] once and stores them to all K destination rows; the
-// workgroup with blockIdx.y == 0 also writes the rows' metadata.
-template <int VPT>
-__global__ __launch_bounds__(kCopyThreads) void dispatch_kernel(CopyParams c, DispatchArgs a) {
+// One workgroup of NT threads per (token, run of columns): each thread loads
+// its VPT vectors of x[t] once and stores them to all K destination rows;
+// the workgroup with blockIdx.y == 0 also writes the rows' metadata.
+template <int VPT, int NT>
+__global__ __launch_bounds__(NT) void dispatch_kernel(CopyParams c, DispatchArgs a) {
     const int t = blockIdx.x;
-    const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    const int v0 = blockIdx.y * (NT * VPT) + threadIdx.x;
     const int32_t lane_slot = a.slot[static_cast<int64_t>(t) * c.K + min(static_cast<int>(__lane_id()), c.K - 1)];
     u32x4 buf[VPT];
-    load_token_row<VPT>(c, a, t, v0, buf);
-    store_token_rows<VPT>(c, a, t, v0, blockIdx.y == 0, lane_slot, buf);
+    load_token_row<VPT, NT>(c, a, t, v0, buf);
+    store_token_rows<VPT, NT>(c, a, t, v0, blockIdx.y == 0, lane_slot, buf);
 }
 
 // e4m3 (OCP "fn": bias 7, 3 mantissa bits, largest finite 448, no
@@ -359,15 +359,23 @@ void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
 }
 
 hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream) {
+    // batches so small that rows split into one-vector pieces take the wider
+    // workgroups of the one-chunk kernel (decode-sized dispatch 0.4 µs faster;
+    // at two or more vectors per thread they were slower)
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, kCopyThreads, &splits, &vpt);
+    const bool wide = vpt == 1;
+    if (wide) copy_grid(c.T, c.nvec, kFusedThreads, &splits, &vpt);
     CopyParams p = c;
     p.vpt = vpt;
     dim3 grid(c.T, splits);
     switch (vpt) {
-#define EP_DISPATCH_CASE(V)                                                \
-    case V:                                                                \
-        dispatch_kernel<V><<<grid, kCopyThreads, 0, stream>>>(p, a);       \
+#define EP_DISPATCH_CASE(V)                                                             \
+    case V:                                                                             \
+        if (wide)                                                                       \
+            dispatch_kernel<V, kFusedThreads><<<grid, kFusedThreads, 0, stream>>>(p, a); \
+        else                                                                            \
+            dispatch_kernel<V, kCopyThreads><<<grid, kCopyThreads, 0, stream>>>(p, a);  \
         break;
         EP_DISPATCH_CASE(1)
         EP_DISPATCH_CASE(2)
