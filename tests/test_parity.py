@@ -368,15 +368,36 @@ def test_device_errors_in_every_layout_mode(ep, T, K, E, R, bad, short):
     assert_layout_matches(ep, bufs, status, ref)
 
 
-def test_repeatable(ep):
-    inp = ep_inputs.make_inputs("zipf8k", with_x=False)
+@pytest.mark.parametrize("name", ["tiny", "decode128", "zipf8k", "large16k"])
+def test_repeatable(ep, name):
+    """Ten runs of the layout (every mode) and of the one-call layout and
+    dispatch with the combine after it give bitwise identical slots, rows and
+    outputs: no atomic decides an order anywhere."""
+    inp = ep_inputs.make_inputs(name)
     wl = inp.wl
     S = oracle.default_rank_stride(wl.T, wl.K, wl.E, wl.R)
     outs = []
-    for _ in range(3):
+    for _ in range(10):
         _, bufs, _ = gpu_layout(ep, inp.topk_idx, wl.E, wl.R, S)
         outs.append(bufs.token_slot.cpu().numpy())
     assert all((o == outs[0]).all() for o in outs)
+    counts = np.bincount(inp.topk_idx.ravel(), minlength=wl.E)
+    S = tight_stride(counts, wl.E, wl.R)
+    p = ep.Problem.make(wl.T, wl.H, wl.E, wl.K, wl.R, wl.G, wl.A, S)
+    bufs = ep.alloc_layout(p)
+    recv = torch.zeros((wl.R * S, wl.H), dtype=torch.int16, device="cuda")
+    out = torch.empty((wl.T, wl.H), dtype=torch.int16, device="cuda")
+    d_idx, d_x, d_w = dev(inp.topk_idx), bf16_dev(inp.x), dev(inp.topk_weights)
+    first = None
+    for _ in range(10):
+        ep.ep_layout_dispatch(p, d_idx, *bufs.args(), None, d_x, d_w, recv)
+        ep.ep_combine(p, recv, bufs.token_slot, d_w, out)
+        got = (bufs.token_slot.clone(), recv.clone(), out.clone())
+        if first is None:
+            first = got
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(first, got))
+    assert ep.ep_read_status(bufs.workspace) == ep.EP_OK
 
 
 def test_bound_calls_repeat_the_direct_calls(ep):
