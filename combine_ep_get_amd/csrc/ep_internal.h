@@ -11,6 +11,10 @@ namespace epget {
 // 64-entry steps when it assigns slots, and the count tables hold one row per
 // chunk, so this trades slot-walk latency against scan-table size.
 constexpr int kChunkEntries = 1024;
+// Largest batch (T * K entries) that the one-call layout and dispatch runs
+// as a single kernel, every dispatching workgroup taking the whole batch's
+// histogram: a few chunks.
+constexpr int kFusedMaxEntries = 4 * kChunkEntries;
 
 // Workspace layout, all offsets in bytes from the workspace base:
 //   [0, 256)                  status word (int32) + padding

@@ -689,9 +689,9 @@ hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
 // earlier duplicates of e inside the token.  Returns slot j in lane j of
 // every wave (j < K), as slot_of reads it.  lds holds 3 * E + 2 ints,
 // s_wsum 2 * NT / 64.  Contains barriers.
-template <int NT>
+template <int NT, int kMaxEntries>
 __device__ __forceinline__ int32_t token_slots_one_chunk(const LayoutParams &p, int t, int *lds, int *s_wsum) {
-    constexpr int kPer = kChunkEntries / NT;
+    constexpr int kPer = kMaxEntries / NT;
     constexpr int kEPT = (EP_MAX_EXPERTS + NT - 1) / NT;
     const int n = p.T * p.K;
     const int tid = threadIdx.x, lane = __lane_id();
@@ -730,6 +730,61 @@ __device__ __forceinline__ int32_t token_slots_one_chunk(const LayoutParams &p, 
     return pos < p.S ? rank * p.S + pos : -1;
 }
 
+// The layout outputs of a batch of at most kFusedMaxEntries entries except
+// the slots, by one workgroup of NT threads that takes the batch chunk by
+// chunk through LDS: with kExperts the per-expert half (counts, aligned
+// offsets, rows per rank, status), with kTokens the per-token half (token-to-
+// rank map, unique tokens per rank and group).  LDS: s_idx [kChunkEntries] |
+// s_hist [pitch] | s_aln [E+1].  Contains barriers.
+template <int NT, bool kExperts, bool kTokens>
+__device__ void fused_layout(const LayoutParams &p, int *lds) {
+    constexpr int kEPT = (EP_MAX_EXPERTS + NT - 1) / NT;
+    __shared__ int s_wsum[2 * NT / 64];
+    __shared__ int s_over;
+    int *s_idx = lds;
+    int *s_hist = s_idx + kChunkEntries;
+    int *s_aln = s_hist + p.pitch;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < p.ncols; i += NT) s_hist[i] = 0;
+    if (tid == 0) s_over = 0;
+    for (int c = 0; c < p.nchunks; ++c) {
+        const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
+        const int n = (t1 - t0) * p.K;
+        __syncthreads();  // the previous chunk is done with s_idx
+        load_ids<NT>(p.topk_idx + static_cast<int64_t>(t0) * p.K, n, s_idx);
+        __syncthreads();
+        entry_pass<NT>(p, n, 1, s_idx, kExperts ? s_hist : nullptr, nullptr);
+        if (kTokens) {
+            __syncthreads();
+            token_pass<NT>(p, t0, t1, s_idx, s_hist);
+        }
+    }
+    __syncthreads();
+    if (kTokens) {
+        for (int i = tid; i < p.R + p.G; i += NT) {
+            const int v = s_hist[p.E + i];
+            if (i < p.R)
+                p.rank_token_count[i] = v;
+            else if (p.group_token_count)
+                p.group_token_count[i - p.R] = v;
+        }
+    }
+    if (!kExperts) return;  // the whole workgroup, after its last barrier
+    for (int e = tid; e < p.E; e += NT) {
+        p.expert_count[e] = s_hist[e];
+        if (p.cumulative) p.cumulative[e] += s_hist[e];
+    }
+    const int bad = s_hist[p.E + p.R + p.G];
+    __syncthreads();  // the counts above are read before the scan rewrites them
+    block_scan_counts<NT, kEPT>(p, s_hist, s_aln, s_hist, s_wsum);
+    __syncthreads();
+    for (int e = tid; e < p.E; e += NT)
+        p.expert_offset[e] = s_aln[e] - s_aln[static_cast<int>(p.div_L(e)) * p.L];
+    if (finish_ranks<NT>(p, s_aln, s_hist)) atomicOr(&s_over, 1);
+    __syncthreads();
+    if (tid == 0) *p.status = status_code(bad > 0, s_over);
+}
+
 // Layout and dispatch in one launch for a batch that is one chunk, on a
 // (T, splits + 1) grid.  Workgroups (0, 0) and (1, 0), dispatched first,
 // compute and write the layout except the slots: the per-expert half
@@ -741,27 +796,36 @@ __device__ __forceinline__ int32_t token_slots_one_chunk(const LayoutParams &p, 
 // workgroups have the linear ids, and so the XCDs, that dispatch_kernel
 // gives them, which the combine's grid shares: rows a small batch leaves in
 // an XCD's L2 are read back there.
-template <int VPT>
+template <int VPT, int kMaxEntries>
 __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutParams p, CopyParams c,
                                                                        DispatchArgs a) {
     extern __shared__ __align__(16) int smem[];
     __shared__ int s_wsum[2 * kFusedThreads / 64];
     if (blockIdx.y == 0) {
         // the layout, split over workgroups (0, 0) and (1, 0) when there are two
-        constexpr int W = kFusedThreads / 64;
-        if (gridDim.x == 1)
-            assign_chunk<W, kFusedChunk, false, kLayoutAll>(p, 0);
-        else if (blockIdx.x == 0)
-            assign_chunk<W, kFusedChunk, false, kLayoutExperts>(p, 0);
-        else if (blockIdx.x == 1)
-            assign_chunk<W, kFusedChunk, false, kLayoutTokens>(p, 0);
+        if constexpr (kMaxEntries == kChunkEntries) {
+            constexpr int W = kFusedThreads / 64;
+            if (gridDim.x == 1)
+                assign_chunk<W, kFusedChunk, false, kLayoutAll>(p, 0);
+            else if (blockIdx.x == 0)
+                assign_chunk<W, kFusedChunk, false, kLayoutExperts>(p, 0);
+            else if (blockIdx.x == 1)
+                assign_chunk<W, kFusedChunk, false, kLayoutTokens>(p, 0);
+        } else {
+            if (gridDim.x == 1)
+                fused_layout<kFusedThreads, true, true>(p, smem);
+            else if (blockIdx.x == 0)
+                fused_layout<kFusedThreads, true, false>(p, smem);
+            else if (blockIdx.x == 1)
+                fused_layout<kFusedThreads, false, true>(p, smem);
+        }
         return;
     }
     const int t = blockIdx.x;
     const int v0 = (blockIdx.y - 1) * (kFusedThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
     load_token_row<VPT, kFusedThreads>(c, a, t, v0, buf);
-    const int32_t lane_slot = token_slots_one_chunk<kFusedThreads>(p, t, smem, s_wsum);
+    const int32_t lane_slot = token_slots_one_chunk<kFusedThreads, kMaxEntries>(p, t, smem, s_wsum);
     const bool meta = blockIdx.y == 1;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
@@ -974,13 +1038,13 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
                                   hipStream_t stream) {
     // the one-chunk kernel has larger workgroups: its slot derivation is on
     // the critical path, and 256 threads share it faster than 128
-    const bool one_chunk = p.T > 0 && p.nchunks == 1;
+    const bool one_chunk = p.T > 0 && static_cast<int64_t>(p.T) * p.K <= kFusedMaxEntries;
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, one_chunk ? kFusedThreads : kCopyThreads, &splits, &vpt);
     CopyParams cp = c;
     cp.vpt = vpt;
     const dim3 grid(c.T, splits + 1);
-    if (p.T > 0 && p.nchunks > 1 && p.nchunks <= kMaxCallChunks && p.A == 1) {
+    if (!one_chunk && p.T > 0 && p.nchunks <= kMaxCallChunks && p.A == 1) {
         // count pass (with the expert-major arrays), then one launch that
         // finishes the layout and dispatches, each workgroup deriving its
         // token's slots
@@ -1012,7 +1076,7 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
         }
         return hipGetLastError();
     }
-    if (p.nchunks != 1 || p.T == 0) {
+    if (!one_chunk) {
         const hipError_t err = launch_layout(p, stream);
         if (err != hipSuccess || p.T == 0) return err;
         return launch_dispatch(c, a, stream);
@@ -1022,9 +1086,12 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
     const size_t lds = sizeof(int) * std::max<size_t>(kChunkEntries + p.pitch + p.E + 1,
                                                       3 * static_cast<size_t>(p.E) + 2);
     switch (vpt) {
-#define EP_LAYOUT_DISPATCH_CASE(V)                                                 \
-    case V:                                                                        \
-        layout_dispatch_kernel<V><<<grid, kFusedThreads, lds, stream>>>(p, cp, a); \
+#define EP_LAYOUT_DISPATCH_CASE(V)                                                                   \
+    case V:                                                                                          \
+        if (p.nchunks == 1)                                                                          \
+            layout_dispatch_kernel<V, kChunkEntries><<<grid, kFusedThreads, lds, stream>>>(p, cp, a); \
+        else                                                                                         \
+            layout_dispatch_kernel<V, kFusedMaxEntries><<<grid, kFusedThreads, lds, stream>>>(p, cp, a); \
         break;
         EP_LAYOUT_DISPATCH_CASE(1)
         EP_LAYOUT_DISPATCH_CASE(2)

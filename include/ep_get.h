@@ -167,10 +167,10 @@ int ep_dispatch(const ep_problem *problem, const uint16_t *x,
  * ep_dispatch on the same stream, with the arguments, outputs, errors and
  * status of both.  [SYM] §6.1 feeds the layout's prefix sums and slots
  * straight into the dispatch launch; here, when the batch is small enough
- * for one layout chunk (T*K <= 1024 after rounding to whole tokens: decode-
- * sized batches), both run as a single kernel in which every dispatching
- * workgroup derives its own token's slots, which saves a launch on the
- * latency-bound path.  Batches of up to 128 chunks of 1024 entries with
+ * for four layout chunks of 1024 entries (T*K <= 4096 after rounding to
+ * whole tokens: decode-sized batches), both run as a single kernel in which
+ * every dispatching workgroup derives its own token's slots, which saves a
+ * launch on the latency-bound path.  Batches of up to 128 chunks with
  * expert_alignment 1 run the count pass and then one kernel that finishes
  * the layout while each dispatching workgroup derives its token's slots from
  * per-chunk counts (two launches instead of three); other batches run the
@@ -240,7 +240,7 @@ int ep_dispatch_fp8(const ep_problem *problem, const uint8_t *x_fp8, const float
 
 /* FP8 layout then dispatch in one call: ep_get_layout followed by
  * ep_dispatch_fp8, with the arguments, outputs, errors and status of both;
- * one kernel when the batch is one layout chunk, as for ep_layout_dispatch
+ * one kernel up to four layout chunks, as for ep_layout_dispatch
  * (decode-sized batches, where [SYM] §9.2's use_fp8_dispatch matters most
  * for latency). */
 int ep_layout_dispatch_fp8(const ep_problem *problem, const int32_t *topk_idx,

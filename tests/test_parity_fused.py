@@ -252,3 +252,34 @@ def test_multi_chunk_wide_top_k(ep, T, K, E, R, G):
     x = ep_inputs.bf16_normal(rng, (T, 64))
     w = rng.random((T, K)).astype(np.float32)
     run_fused(ep, idx, w, x, E, R, G, S=tight_stride(counts, E, R), cumulative=True)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_few_chunk_single_kernel(ep, seed):
+    """Batches of two to four chunks run as a single kernel (the layout
+    workgroups take the batch chunk by chunk): alignment, slices one row
+    short, bad and empty ids, duplicates, groups, R above a wave."""
+    rng = np.random.default_rng(3000 + seed)
+    R = int(rng.choice([2, 8, 96, 128]))
+    L = int(rng.choice([1, 2, 4]))
+    E = R * L
+    K = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(1024 // K + 1, 4096 // K + 1))
+    G = int(rng.choice([g for g in (1, 2, 4) if R % g == 0]))
+    A = int(rng.choice([1, 1, 2, 3]))
+    if seed % 2:
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    else:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    idx[rng.random((T, K)) < 0.05] = -1
+    if seed % 3 == 0:
+        idx[rng.integers(0, T, 2), rng.integers(0, K, 2)] = E + 1
+    S = None
+    if seed % 4 == 1:
+        ok = (idx >= 0) & (idx < E)
+        S = tight_stride(np.bincount(idx[ok], minlength=E), E, R, A) - 1
+    x = ep_inputs.bf16_normal(rng, (T, 64))
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    ref, _ = run_fused(ep, idx, w, x, E, R, G, A, S=S, cumulative=seed % 3 == 1)
+    if S is not None and ref.status != oracle.BAD_EXPERT:
+        assert ref.status == oracle.CAPACITY
