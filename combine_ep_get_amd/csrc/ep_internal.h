@@ -98,7 +98,7 @@ struct HierParams {
 };
 
 constexpr int kCopyThreads = 128;      // dispatch workgroup size
-constexpr int kFusedThreads = 256;     // workgroup of the one-chunk layout + dispatch kernel
+constexpr int kFusedThreads = 256;     // workgroup of the single-kernel layout + dispatch
 constexpr int kMaxVpt = 8;            // dispatch vectors per thread
 constexpr int kCombineMaxThreads = 1024;
 

@@ -31,9 +31,10 @@
 // Single-chunk path (one launch, batches of up to kChunkEntries entries): the
 // assign workgroup also builds the histogram and writes the counts, and a
 // second workgroup writes the token-to-rank map and unique-token counts.
-// Layout and dispatch in one launch (one-chunk batches): two workgroups
-// write the layout outputs while every dispatching workgroup derives its own
-// token's slots from LDS histograms of the batch (layout_dispatch_kernel).
+// Layout and dispatch in one launch (batches of up to kFusedMaxEntries
+// entries): two workgroups write the layout outputs while every dispatching
+// workgroup derives its own token's slots from LDS histograms of the batch
+// (layout_dispatch_kernel).
 // Up to kMaxCallChunks chunks with A = 1: the count pass, then one launch
 // that does the same from expert-major per-chunk counts
 // (dispatch_chunks_kernel).
@@ -678,9 +679,9 @@ hipError_t launch_assign(const LayoutParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Slots of token t's K entries when the whole batch is one chunk
-// (T * K <= kChunkEntries), found by one workgroup of NT threads without the
-// slot walk.  Entry (t, j) with expert e lands at row
+// Slots of token t's K entries when the whole batch has at most kMaxEntries
+// (a multiple of NT, at most kFusedMaxEntries) entries, found by one
+// workgroup of NT threads without the slot walk.  Entry (t, j) with expert e lands at row
 //   expert_offset[e] + #{entries before (t, j) naming e}
 // of its rank's slice, which is the slot the walk assigns.  The workgroup
 // builds two LDS histograms of the batch, one over all entries and one over
@@ -785,12 +786,13 @@ __device__ void fused_layout(const LayoutParams &p, int *lds) {
     if (tid == 0) *p.status = status_code(bad > 0, s_over);
 }
 
-// Layout and dispatch in one launch for a batch that is one chunk, on a
-// (T, splits + 1) grid.  Workgroups (0, 0) and (1, 0), dispatched first,
-// compute and write the layout except the slots: the per-expert half
-// (counts, offsets, rank rows, status) and the per-token half (token-to-rank
-// map, unique tokens per rank and group); the rest of row y = 0 has nothing
-// to do.  Workgroup
+// Layout and dispatch in one launch for a batch of at most kMaxEntries
+// entries (one chunk, or up to kFusedMaxEntries), on a (T, splits + 1)
+// grid.  Workgroups (0, 0) and (1, 0), dispatched first, compute and write
+// the layout except the slots: the per-expert half (counts, offsets, rank
+// rows, status) and the per-token half (token-to-rank map, unique tokens per
+// rank and group), over one chunk in LDS or chunk by chunk; the rest of row
+// y = 0 has nothing to do.  Workgroup
 // (t, y > 0) finds the slots of token t itself, writes them to token_slot if
 // y == 1, and dispatches column run y - 1 of the token's row.  Token t's
 // workgroups have the linear ids, and so the XCDs, that dispatch_kernel
@@ -1036,8 +1038,8 @@ hipError_t launch_layout(const LayoutParams &lp, hipStream_t stream) {
 
 hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, const DispatchArgs &a,
                                   hipStream_t stream) {
-    // the one-chunk kernel has larger workgroups: its slot derivation is on
-    // the critical path, and 256 threads share it faster than 128
+    // the single-kernel form has larger workgroups: its slot derivation is
+    // on the critical path, and 256 threads share it faster than 128
     const bool one_chunk = p.T > 0 && static_cast<int64_t>(p.T) * p.K <= kFusedMaxEntries;
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, one_chunk ? kFusedThreads : kCopyThreads, &splits, &vpt);

@@ -359,9 +359,10 @@ void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
 }
 
 hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream) {
-    // batches so small that rows split into one-vector pieces take the wider
-    // workgroups of the one-chunk kernel (decode-sized dispatch 0.4 µs faster;
-    // at two or more vectors per thread they were slower)
+    // batches so small that rows split into one-vector pieces take the
+    // wider workgroups of the single-kernel layout + dispatch (decode-sized
+    // dispatch 0.4 µs faster; at two or more vectors per thread they were
+    // slower)
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, kCopyThreads, &splits, &vpt);
     const bool wide = vpt == 1;
