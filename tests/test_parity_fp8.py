@@ -182,3 +182,38 @@ def test_fp8_rejects_hidden_not_multiple_of_128(ep):
     p = ep.Problem.make(16, 200, 8, 2, 2, 1, 1, 64)
     with pytest.raises(ep.EpError):
         ep.ep_quantize_fp8(p, 1 << 20, 1 << 20, 1 << 20)
+
+
+@pytest.mark.parametrize("T,K,column_major", [(300, 8, False), (500, 8, True), (2000, 3, False)])
+def test_layout_dispatch_fp8_few_chunks(ep, T, K, column_major):
+    """The one-call FP8 path on two to six chunks: the single kernel up to
+    four chunks, the count pass and one kernel beyond."""
+    rng = np.random.default_rng(T + K)
+    E, R, H = 64, 8, 1024
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    w = rng.random((T, K)).astype(np.float32)
+    S = oracle.default_rank_stride(T, K, E, R)
+    rows = R * S
+    lay = oracle.layout(idx, E, R, S, 1)
+    q, sf = oracle.quantize_fp8(x)
+    rq, rsf, (ts, hs), rsrc, rw = oracle.dispatch_fp8(q, sf, lay.token_slot, rows, w,
+                                                     column_major_sf=column_major)
+    p = ep.Problem.make(T, H, E, K, R, 1, 1, S)
+    bufs = ep.alloc_layout(p)
+    g_q = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+    g_sf = torch.full((rsf.size,), float("nan"), dtype=torch.float32, device="cuda")
+    g_src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ep.ep_layout_dispatch_fp8(p, dev(idx), *bufs.args(), None, dev(q), dev(sf), dev(w), g_q, g_sf, ts, hs,
+                              g_src, g_w)
+    assert ep.ep_read_status(bufs.workspace) == ep.EP_OK
+    assert_same(bufs.token_slot.cpu().numpy(), lay.token_slot, "token_slot")
+    assert_same(bufs.is_token_in_rank.cpu().numpy(), lay.is_token_in_rank, "is_token_in_rank")
+    s = lay.token_slot.ravel()
+    assert_same(g_q.cpu().numpy()[s], rq[s])
+    nb = H // 128
+    sel = (s[:, None] * ts + np.arange(nb)[None, :] * hs).ravel()
+    assert_same(g_sf.cpu().numpy()[sel], rsf[sel])
+    assert_same(g_src.cpu().numpy()[s], rsrc[s])
+    assert_same(g_w.cpu().numpy()[s], rw[s])
