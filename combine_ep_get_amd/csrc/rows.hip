@@ -278,46 +278,6 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, Hier
     }
 }
 
-// Group slots: a stable compaction, per group, of the tokens with an entry on
-// one of the group's ranks.  One workgroup per group walks the tokens in
-// tiles of kGroupThreads; a thread reads its token's rank bytes, and a
-// workgroup scan (DPP inside waves, wave totals through LDS) gives positions.
-constexpr int kGroupThreads = 1024;
-
-__global__ __launch_bounds__(kGroupThreads) void group_layout_kernel(int32_t T, int32_t R, HierParams h,
-                                                                     const uint8_t *__restrict__ map,
-                                                                     int32_t *__restrict__ group_slot) {
-    __shared__ int s_wsum[kGroupThreads / 64];
-    const int g = blockIdx.x;
-    const int lane = __lane_id(), w = threadIdx.x >> 6;
-    const int r0 = g * h.ranks_per_group;
-    int carry = 0;
-    for (int base = 0; base < T; base += kGroupThreads) {
-        const int t = base + threadIdx.x;
-        const int tc = min(t, T - 1);
-        const uint8_t *row = map + static_cast<int64_t>(tc) * R + r0;
-        int in = 0;
-        for (int r = 0; r < h.ranks_per_group; ++r) in |= row[r];
-        in = (t < T && in) ? 1 : 0;
-        const int incl = wave_inclusive_sum(in);
-        if (lane == 63) s_wsum[w] = incl;
-        __syncthreads();
-        int before = 0, total = 0;
-#pragma unroll
-        for (int i = 0; i < kGroupThreads / 64; ++i) {
-            const int v = s_wsum[i];
-            before += i < w ? v : 0;
-            total += v;
-        }
-        if (t < T) {
-            const int pos = carry + before + incl - in;
-            group_slot[static_cast<int64_t>(t) * h.G + g] = (in && pos < h.SG) ? g * h.SG + pos : -1;
-        }
-        carry += total;
-        __syncthreads();
-    }
-}
-
 // combined_topk_weights: one thread per (token, top-k) entry.
 __global__ __launch_bounds__(256) void combine_weights_kernel(CopyParams c, const float *__restrict__ recv_w,
                                                               const int32_t *__restrict__ slot,
@@ -422,12 +382,6 @@ hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, cons
                                   float *combined_w, hipStream_t stream) {
     const int64_t n = static_cast<int64_t>(c.T) * c.K;
     combine_weights_kernel<<<(n + 255) / 256, 256, 0, stream>>>(c, recv_w, slot, combined_w);
-    return hipGetLastError();
-}
-
-hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
-                               int32_t *group_slot, hipStream_t stream) {
-    group_layout_kernel<<<h.G, kGroupThreads, 0, stream>>>(T, R, h, map, group_slot);
     return hipGetLastError();
 }
 

@@ -103,3 +103,31 @@ def test_hier_small_group_capacity_and_empty_entries(ep):
     ref = oracle.layout(idx, E, R, S, G)
     SG = int(ref.group_token_count.min()) - 10   # the later tokens of each group are dropped
     run(ep, idx, w, x, E, R, G, S, SG)
+
+
+@pytest.mark.parametrize("T,R,G,density,offset", [
+    (40000, 8, 2, 0.3, 0),     # three passes of 16384 tokens, ragged tail; words of 4 ranks
+    (16384, 16, 2, 0.05, 0),   # one full pass; two words per group
+    (16385, 12, 4, 0.2, 0),    # one token past a pass; three rank bytes per group
+    (33000, 8, 8, 0.1, 0),     # one rank per group
+    (20000, 8, 1, 0.02, 0),    # a single group of all ranks
+    (5000, 8, 2, 0.3, 1),      # map not 4-byte aligned: bytes even though 4 ranks per group
+    (1024, 8, 2, 0.5, 0),      # the largest batch for 64-thread workgroups, one full pass
+    (4097, 8, 4, 0.3, 0),      # one token past the 256-thread workgroups' pass
+    (1, 4, 1, 1.0, 0),
+])
+def test_group_layout_maps(ep, T, R, G, density, offset):
+    """ep_get_group_layout on synthetic maps, apart from ep_get_layout: any
+    nonzero byte marks the rank, rows with no rank anywhere occur, and the
+    per-group capacity drops the later tokens of the fuller groups."""
+    print(f"[parity-hier] group layout T={T} R={R} G={G} offset={offset}", flush=True)
+    rng = np.random.default_rng(T + 7 * R + G)
+    m = np.where(rng.random((T, R)) < density, rng.integers(1, 256, (T, R)), 0).astype(np.uint8)
+    p = ep.Problem.make(T, 8, 8 * R, 1, R, G, 1, 1)
+    for SG in (T, max(1, int(density * T * (R // G) * 0.5))):
+        flat = torch.zeros(T * R + offset, dtype=torch.uint8, device="cuda")
+        flat[offset:] = dev(m.ravel())
+        gslot = torch.empty((T, G), dtype=torch.int32, device="cuda")
+        ep.ep_get_group_layout(p, flat[offset:].view(T, R), SG, gslot)
+        torch.cuda.synchronize()
+        assert_same(gslot.cpu().numpy(), oracle.group_layout(m, G, SG), f"SG={SG}")
