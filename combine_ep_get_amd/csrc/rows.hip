@@ -217,7 +217,11 @@ struct GroupOf {
 
 // Two-level combine, stage 1: for each group the token reaches, the partial
 // sum over the token's entries in that group, rounded to bf16 into the
-// group buffer row group_slot[t,g].
+// group buffer row group_slot[t,g].  With K <= KG the K rows are loaded once
+// and each group folds its own entries from registers (ascending j, as in
+// gather_fold); gathering per group instead kept half as many loads in
+// flight and loaded row 0 for the other groups' entries: 18 µs slower on a
+// 4096-token step with four groups, 22 µs on 16384 tokens with two.
 template <int KG>
 __global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
     CopyParams c, HierParams h, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
@@ -228,6 +232,41 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
     const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
     const int col = blockIdx.y * blockDim.x + threadIdx.x;
     const int colc = min(col, c.nvec - 1);
+    if (c.K <= KG) {
+        // all K rows in flight once, then folded group by group from registers
+        u32x4 in[KG];
+        int32_t grp[KG];
+        float wj[KG];
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+            const int j = min(jj, c.K - 1);
+            const int32_t s = srow[j];
+            const bool ok = jj < c.K && slot_ok(s, c.num_rows);
+            grp[jj] = ok ? (s / h.S) / h.ranks_per_group : -1;
+            wj[jj] = wrow ? wrow[j] : 1.0f;
+            const int64_t row = ok ? s : 0;
+            in[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + row * c.H) + colc);
+        }
+        for (int g = 0; g < h.G; ++g) {
+            const int32_t gs = group_slot[static_cast<int64_t>(t) * h.G + g];
+            if (gs < 0 || gs >= h.group_rows) continue;
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = __builtin_fmaf(wj[jj], bf16_lo(in[jj][q]), acc[2 * q]);
+                    const float hi = __builtin_fmaf(wj[jj], bf16_hi(in[jj][q]), acc[2 * q + 1]);
+                    acc[2 * q] = grp[jj] == g ? lo : acc[2 * q];
+                    acc[2 * q + 1] = grp[jj] == g ? hi : acc[2 * q + 1];
+                }
+            }
+            if (col < c.nvec) reinterpret_cast<u32x4 *>(group_buf + static_cast<int64_t>(gs) * c.H)[col] = pack_row(acc);
+        }
+        return;
+    }
     for (int g = 0; g < h.G; ++g) {
         const int32_t gs = group_slot[static_cast<int64_t>(t) * h.G + g];
         if (gs < 0 || gs >= h.group_rows) continue;

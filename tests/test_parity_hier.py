@@ -105,6 +105,22 @@ def test_hier_small_group_capacity_and_empty_entries(ep):
     run(ep, idx, w, x, E, R, G, S, SG)
 
 
+@pytest.mark.parametrize("K,G", [(1, 2), (3, 4), (4, 2), (8, 8), (9, 2), (12, 4)])
+def test_hier_topk_widths(ep, K, G):
+    """Partial combine with the K rows gathered once (K <= 8: one or two
+    groups' folds from registers) and, past 8, gathered group by group."""
+    print(f"[parity-hier] K={K} G={G}", flush=True)
+    rng = np.random.default_rng(100 + K * G)
+    T, E, R, H = 700, 64, 8, 264
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.05] = -1
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    counts = np.bincount(idx[idx >= 0], minlength=E)
+    S = int(counts.reshape(R, -1).sum(1).max())
+    run(ep, idx, w, x, E, R, G, S, T)
+
+
 @pytest.mark.parametrize("T,R,G,density,offset", [
     (40000, 8, 2, 0.3, 0),     # three passes of 16384 tokens, ragged tail; words of 4 ranks
     (16384, 16, 2, 0.05, 0),   # one full pass; two words per group
