@@ -32,7 +32,9 @@ int check_shape(const ep_problem *p) {
     if (p->expert_alignment < 1) return EP_ERR_INVALID_ARG;
     const int64_t entries = static_cast<int64_t>(p->num_tokens) * p->num_topk;
     const int64_t pad = static_cast<int64_t>(p->num_experts) * p->expert_alignment;
-    if (entries + pad > INT32_MAX) return EP_ERR_INVALID_ARG;
+    // index arithmetic in the kernels overshoots the last entry or token by
+    // less than a tile (at most 16384) before it is clamped or tested
+    if (entries + pad > INT32_MAX - (1 << 16)) return EP_ERR_INVALID_ARG;
     return EP_OK;
 }
 

@@ -73,7 +73,8 @@ extern "C" {
  *   1 <= E <= 2048; 1 <= R <= 1024; E % R == 0; E / R <= 256;
  *   1 <= G and R % G == 0; 1 <= K <= 32; A >= 1;
  *   S >= 1; R * S <= INT32_MAX (slots are int32);
- *   T * K + E * A <= INT32_MAX. */
+ *   T * K + E * A <= INT32_MAX - 65536 (entry and token indices stay int32
+ *   with room for the kernels' tiles to run past the end before clamping). */
 typedef struct ep_problem {
     int32_t num_tokens;       /* T: tokens of this source rank */
     int32_t hidden;           /* H: bf16 elements per row, a multiple of 8, <= EP_MAX_HIDDEN */

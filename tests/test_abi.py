@@ -47,12 +47,16 @@ def test_stride_hint_and_workspace():
     assert ep.ep_rank_stride_hint(P(A=8)) == 4096 * 8 + 32 * 7
     assert ep.ep_workspace_bytes(P()) > 0
     assert ep.ep_workspace_bytes(P(T=0)) > 0
+    # the largest batch: T*K + E*A = INT32_MAX - 65536 at most
+    assert ep.ep_workspace_bytes(P(T=(2**31 - 1 - 2**16 - 256) // 8, S=1)) > 0
+    assert ep.ep_workspace_bytes(P(T=(2**31 - 1 - 2**16 - 256) // 8 + 1, S=1)) == 0
 
 
 @pytest.mark.parametrize("bad", [
     dict(E=255), dict(E=4096, R=8), dict(R=2048, E=2048), dict(E=1024, R=2),   # limits
     dict(K=0), dict(K=33), dict(H=7), dict(H=0), dict(H=(1 << 24) + 8), dict(T=-1), dict(G=3), dict(G=0),
     dict(A=0), dict(S=0), dict(S=2**31 // 8 + 1),
+    dict(T=(2**31 - 1 - 2**16 - 256) // 8 + 1, S=1),      # T*K + E*A one tile short of int32
 ])
 def test_invalid_problems_rejected_before_launch(bad):
     p = P(**bad)
