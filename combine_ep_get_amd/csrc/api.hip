@@ -364,14 +364,7 @@ int ep_dispatch_hier(const ep_problem *p, const uint16_t *x, const float *topk_w
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const epget::HierParams h = hier_params(p, group_stride_rows);
     // stage 1: each token once to every group it reaches
-    epget::CopyParams c1 = copy_params(p);
-    c1.K = h.G;
-    c1.num_rows = h.group_rows;
-    epget::DispatchArgs a1 = {};
-    a1.x = x;
-    a1.slot = group_slot;
-    a1.recv = group_buf;
-    hipError_t err = epget::launch_dispatch(c1, a1, st);
+    hipError_t err = epget::launch_group_dispatch(copy_params(p), h, x, group_slot, group_buf, st);
     if (err != hipSuccess) return EP_ERR_HIP;
     // stage 2: group rows to the entries' rows
     epget::DispatchArgs a2 = {};
@@ -400,11 +393,8 @@ int ep_combine_hier(const ep_problem *p, const uint16_t *y, const int32_t *token
     hipError_t err = epget::launch_combine_partial(copy_params(p), h, y, token_slot, topk_weights,
                                                    group_slot, group_buf, st);
     if (err != hipSuccess) return EP_ERR_HIP;
-    // stage 2: sum of the token's group rows (unit weights)
-    epget::CopyParams c2 = copy_params(p);
-    c2.K = h.G;
-    c2.num_rows = h.group_rows;
-    return hip_rc(epget::launch_combine(c2, group_buf, group_slot, nullptr, out, st));
+    // stage 2: sum of the token's group rows
+    return hip_rc(epget::launch_combine_groups(copy_params(p), h, group_buf, group_slot, out, st));
 }
 
 int ep_read_status(const void *workspace, void *stream) {

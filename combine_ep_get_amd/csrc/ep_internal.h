@@ -114,6 +114,12 @@ hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t 
                           const float *w, uint16_t *out, hipStream_t stream);
 hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
                                int32_t *group_slot, hipStream_t stream);
+// Two-level stages: each token's row to its group rows (stage-1 dispatch)
+// and the sum of a token's group rows (stage-2 combine).
+hipError_t launch_group_dispatch(const CopyParams &c, const HierParams &h, const uint16_t *x,
+                                 const int32_t *group_slot, uint16_t *group_buf, hipStream_t stream);
+hipError_t launch_combine_groups(const CopyParams &c, const HierParams &h, const uint16_t *group_buf,
+                                 const int32_t *group_slot, uint16_t *out, hipStream_t stream);
 hipError_t launch_expand(const CopyParams &c, const HierParams &h, const DispatchArgs &a,
                          const int32_t *group_slot, const uint16_t *group_buf, hipStream_t stream);
 hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, const uint16_t *y,

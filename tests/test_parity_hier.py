@@ -121,6 +121,29 @@ def test_hier_topk_widths(ep, K, G):
     run(ep, idx, w, x, E, R, G, S, T)
 
 
+@pytest.mark.parametrize("E,R,G,K", [
+    (256, 16, 16, 8),    # the fewest groups that take the ballot walk
+    (256, 32, 16, 12),   # and top-k past 8 (the partial combine gathers per group)
+    (256, 128, 64, 8),   # one wave's worth of groups
+    (260, 130, 65, 8),   # one group past it: a second ballot round with one lane
+    (1920, 192, 96, 8),  # two ranks per group
+    (2048, 1024, 128, 8),  # eight ranks per group, the largest R
+    (1024, 1024, 1024, 8),  # one rank per group
+])
+def test_hier_many_groups(ep, E, R, G, K):
+    """More than eight groups: every two-level stage finds the token's group
+    rows with a ballot over 64 groups at a time (past 64, in several rounds)."""
+    print(f"[parity-hier] E={E} R={R} G={G} K={K}", flush=True)
+    rng = np.random.default_rng(E + R + G + K)
+    T, H = 300, 64
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    counts = np.bincount(idx.ravel(), minlength=E)
+    S = max(1, int(counts.reshape(R, -1).sum(1).max()))
+    run(ep, idx, w, x, E, R, G, S, T)
+
+
 @pytest.mark.parametrize("T,R,G,density,offset", [
     (40000, 8, 2, 0.3, 0),     # three passes of 16384 tokens, ragged tail; words of 4 ranks
     (16384, 16, 2, 0.05, 0),   # one full pass; two words per group
@@ -130,6 +153,7 @@ def test_hier_topk_widths(ep, K, G):
     (5000, 8, 2, 0.3, 1),      # map not 4-byte aligned: bytes even though 4 ranks per group
     (1024, 8, 2, 0.5, 0),      # the largest batch for 64-thread workgroups, one full pass
     (4097, 8, 4, 0.3, 0),      # one token past the 256-thread workgroups' pass
+    (3000, 1024, 128, 0.005, 0),  # more groups than a wave has lanes
     (1, 4, 1, 1.0, 0),
 ])
 def test_group_layout_maps(ep, T, R, G, density, offset):
@@ -139,7 +163,7 @@ def test_group_layout_maps(ep, T, R, G, density, offset):
     print(f"[parity-hier] group layout T={T} R={R} G={G} offset={offset}", flush=True)
     rng = np.random.default_rng(T + 7 * R + G)
     m = np.where(rng.random((T, R)) < density, rng.integers(1, 256, (T, R)), 0).astype(np.uint8)
-    p = ep.Problem.make(T, 8, 8 * R, 1, R, G, 1, 1)
+    p = ep.Problem.make(T, 8, R * min(8, 2048 // R), 1, R, G, 1, 1)   # E <= 2048
     for SG in (T, max(1, int(density * T * (R // G) * 0.5))):
         flat = torch.zeros(T * R + offset, dtype=torch.uint8, device="cuda")
         flat[offset:] = dev(m.ravel())
