@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libepget.so")
-SOURCES = ["api.hip", "layout.hip", "rows.hip", "groups.hip"]
+SOURCES = ["api.hip", "layout.hip", "rows.hip", "hier.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -10,6 +10,7 @@
 
 #include "../../include/ep_get.h"
 #include "ep_internal.h"
+#include "hier_internal.h"
 
 namespace {
 

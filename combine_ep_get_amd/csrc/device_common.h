@@ -1,5 +1,6 @@
-// Device helpers shared by the layout and row kernels of libepget: wave64
-// prefix sums and the 16-byte row copy of dispatch.  Internal header.
+// Device helpers shared by the kernels of libepget: wave64 prefix sums, the
+// 16-byte row copy of dispatch, and the gather-and-fold of combine with its
+// bf16 packing.  Internal header.
 #pragma once
 
 #include "ep_internal.h"
@@ -97,6 +98,62 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
         }
         if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
+}
+
+// The two bf16 values packed in a 32-bit word, as fp32 (low half, high half).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Two fp32 values rounded to bf16 (nearest even) and packed, lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = static_cast<__bf16>(lo);
+    const __bf16 b = static_cast<__bf16>(hi);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// Folds the top-k rows of one token at 16-byte column colc into acc, in
+// ascending j with fp32 FMA, for the entries whose slot is valid and passes
+// keep(slot).  KG entries are gathered per round, all KG loads in flight; an
+// entry that does not count loads row 0 instead (always in bounds) and is
+// discarded by a select, so no load sits behind a branch.  The rows are read
+// once, so the loads carry the non-temporal hint.
+template <int KG, class Keep>
+__device__ __forceinline__ void gather_fold(const CopyParams &c, const uint16_t *__restrict__ y,
+                                            const int32_t *srow, const float *wrow, int colc,
+                                            Keep keep, float acc[8]) {
+    for (int j0 = 0; j0 < c.K; j0 += KG) {
+        u32x4 in[KG];
+        bool ok[KG];
+        float wj[KG];
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+            const int j = min(j0 + jj, c.K - 1);
+            const int32_t s = srow[j];
+            ok[jj] = j0 + jj < c.K && slot_ok(s, c.num_rows) && keep(s);
+            wj[jj] = wrow ? wrow[j] : 1.0f;
+            const int64_t row = ok[jj] ? s : 0;
+            in[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + row * c.H) + colc);
+        }
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = __builtin_fmaf(wj[jj], bf16_lo(in[jj][q]), acc[2 * q]);
+                const float hi = __builtin_fmaf(wj[jj], bf16_hi(in[jj][q]), acc[2 * q + 1]);
+                acc[2 * q] = ok[jj] ? lo : acc[2 * q];
+                acc[2 * q + 1] = ok[jj] ? hi : acc[2 * q + 1];
+            }
+        }
+    }
+}
+
+// Eight fp32 accumulators as one 16-byte vector of bf16.
+__device__ __forceinline__ u32x4 pack_row(const float acc[8]) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    return o;
 }
 
 }  // namespace

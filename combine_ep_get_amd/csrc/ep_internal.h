@@ -90,13 +90,6 @@ struct DispatchArgs {
     int32_t nsf;
 };
 
-// Two-level (group) path: G groups of ranks_per_group ranks, rank slices of
-// S rows, group slices of SG rows (group_rows = G * SG).
-struct HierParams {
-    int32_t G, ranks_per_group, S, SG;
-    int64_t group_rows;
-};
-
 constexpr int kCopyThreads = 128;      // dispatch workgroup size
 constexpr int kFusedThreads = 256;     // workgroup of the single-kernel layout + dispatch
 constexpr int kMaxVpt = 8;            // dispatch vectors per thread
@@ -112,19 +105,6 @@ hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t 
                                hipStream_t stream);
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
                           const float *w, uint16_t *out, hipStream_t stream);
-hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
-                               int32_t *group_slot, hipStream_t stream);
-// Two-level stages: each token's row to its group rows (stage-1 dispatch)
-// and the sum of a token's group rows (stage-2 combine).
-hipError_t launch_group_dispatch(const CopyParams &c, const HierParams &h, const uint16_t *x,
-                                 const int32_t *group_slot, uint16_t *group_buf, hipStream_t stream);
-hipError_t launch_combine_groups(const CopyParams &c, const HierParams &h, const uint16_t *group_buf,
-                                 const int32_t *group_slot, uint16_t *out, hipStream_t stream);
-hipError_t launch_expand(const CopyParams &c, const HierParams &h, const DispatchArgs &a,
-                         const int32_t *group_slot, const uint16_t *group_buf, hipStream_t stream);
-hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, const uint16_t *y,
-                                  const int32_t *slot, const float *w, const int32_t *group_slot,
-                                  uint16_t *group_buf, hipStream_t stream);
 hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, const int32_t *slot,
                                   float *combined_w, hipStream_t stream);
 

@@ -1,0 +1,457 @@
+// Two-level (hierarchical) path for gfx950: group slots, the group stage of
+// dispatch and combine, and the expansion inside a group.
+//
+// "DeepEP V2 ElasticBuffer 架构深度分析" (hybrid dispatch; logical topology
+// block) and "第 3 章 V1：Buffer 初始化与通信域建立" §3.2 (ranks grouped by
+// eight) send a token once to every scale-out group it reaches and expand
+// it inside the group.  The group stage needs, per group, the row of each
+// such token in the group buffer: a stable compaction of the tokens whose
+// is_token_in_rank bytes are nonzero on any of the group's ranks, capped at
+// the group's SG rows.  The combine mirrors it: per (token, group) the
+// partial sum of the token's entries in the group, rounded to bf16 (what
+// would cross the scale-out link), then the sum of the group rows.
+#include "../../include/ep_get.h"
+#include "device_common.h"
+#include "hier_internal.h"
+
+namespace epget {
+namespace {
+
+// Group slots.  One workgroup of NT threads per group takes the tokens in
+// passes of NT * kGroupTpt.  In a pass, thread i first reads the rank bytes
+// of tokens i, i + NT, i + 2 NT, ... (neighbouring lanes read neighbouring
+// rows) and leaves a 0/1 flag per token in LDS; it then owns kGroupTpt
+// consecutive flags, counts them, and a workgroup scan (DPP inside waves,
+// wave totals through LDS) gives each thread its first position; the slots
+// are written back in the first order, so the stores of a wave also cover
+// neighbouring rows.  The launch picks the smallest NT whose pass holds the
+// batch (up to 16384 tokens), so a batch pays its load latency once.
+constexpr int kGroupTpt = 16;  // flags per thread in the scan
+
+// kWords: the group's rank bytes are read four at a time (ranks per group a
+// multiple of 4 and the map 4-byte aligned, so every word is aligned).
+template <bool kWords, int NT>
+__global__ __launch_bounds__(NT) void group_layout_kernel(int32_t T, int32_t R, HierParams h,
+                                                          const uint8_t *__restrict__ map,
+                                                          int32_t *__restrict__ group_slot) {
+    constexpr int kPass = NT * kGroupTpt;
+    __shared__ __align__(16) uint8_t s_flag[kPass];
+    __shared__ int s_first[NT];
+    __shared__ uint32_t s_bits[NT];
+    __shared__ int s_wsum[NT / 64];
+    const int g = blockIdx.x;
+    const int i = threadIdx.x, lane = __lane_id(), w = i >> 6;
+    const int r0 = g * h.ranks_per_group;
+    int carry = 0;
+    for (int base = 0; base < T; base += kPass) {
+        uint32_t in[kGroupTpt];
+#pragma unroll
+        for (int k = 0; k < kGroupTpt; ++k) in[k] = 0;
+        // rank by rank (word by word), so the loads of all the tokens issue
+        // together; a k whose NT tokens all lie past T loads nothing
+        for (int r = 0; r < h.ranks_per_group; r += kWords ? 4 : 1) {
+#pragma unroll
+            for (int k = 0; k < kGroupTpt; ++k) {
+                if (base + k * NT >= T) break;
+                const int t = min(base + i + k * NT, T - 1);
+                const uint8_t *b = map + static_cast<int64_t>(t) * R + r0 + r;
+                in[k] |= kWords ? *reinterpret_cast<const uint32_t *>(b) : *b;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kGroupTpt; ++k) s_flag[i + k * NT] = (base + i + k * NT < T && in[k]) ? 1 : 0;
+        __syncthreads();
+        // flags base + i*kGroupTpt ... as bits: byte b of a word is bit 8b
+        const u32x4 f = *reinterpret_cast<const u32x4 *>(s_flag + i * kGroupTpt);
+        uint32_t bits = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t v = f[q];
+            bits |= ((v & 1u) | ((v >> 7) & 2u) | ((v >> 14) & 4u) | ((v >> 21) & 8u)) << (4 * q);
+        }
+        const int n = __popc(bits);
+        const int incl = wave_inclusive_sum(n);
+        if (lane == 63) s_wsum[w] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int q = 0; q < NT / 64; ++q) {
+            const int v = s_wsum[q];
+            before += q < w ? v : 0;
+            total += v;
+        }
+        s_first[i] = carry + before + incl - n;
+        s_bits[i] = bits;
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < kGroupTpt; ++k) {
+            if (base + k * NT >= T) break;
+            const int e = i + k * NT;  // token base + e, owned by thread e / kGroupTpt
+            const int t = base + e;
+            if (t < T) {
+                const uint32_t ob = s_bits[e / kGroupTpt];
+                const int b = e % kGroupTpt;
+                const int pos = s_first[e / kGroupTpt] + __popc(ob & ((1u << b) - 1u));
+                group_slot[static_cast<int64_t>(t) * h.G + g] =
+                    ((ob >> b) & 1u) && pos < h.SG ? g * h.SG + pos : -1;
+            }
+        }
+        carry += total;
+        __syncthreads();  // LDS is rewritten by the next pass
+    }
+}
+
+template <bool kWords>
+void launch_group_layout_nt(int32_t T, int32_t R, const HierParams &h, const uint8_t *map, int32_t *group_slot,
+                            hipStream_t stream) {
+    if (T <= 64 * kGroupTpt)
+        group_layout_kernel<kWords, 64><<<h.G, 64, 0, stream>>>(T, R, h, map, group_slot);
+    else if (T <= 256 * kGroupTpt)
+        group_layout_kernel<kWords, 256><<<h.G, 256, 0, stream>>>(T, R, h, map, group_slot);
+    else
+        group_layout_kernel<kWords, 1024><<<h.G, 1024, 0, stream>>>(T, R, h, map, group_slot);
+}
+
+// Group of a valid entry slot in the two-level path: rank = slot / S,
+// group = rank / (R / G).
+struct GroupOf {
+    int32_t S, ranks_per_group, g;
+    __device__ bool operator()(int32_t s) const { return (s / S) / ranks_per_group == g; }
+};
+
+// Calls f(g, gs) for each group g, in ascending order, whose slot
+// gs = gsrow[g] is a group row (0 <= gs < G*SG).  With few groups (kWide
+// false) the slots are read one by one through the scalar cache.  With many,
+// lane l of a wave reads the slot of group g0 + l and a ballot marks the
+// valid ones, so a token costs one load per 64 groups and one step per group
+// it reaches, whatever G is; the mask is wave-uniform, and every lane of the
+// wave must take part.  The two forms are separate instantiations: the wide
+// one holds more registers, which the few-group kernels cannot spare.
+constexpr int kNarrowGroups = 8;  // the largest G that takes the scalar walk
+
+template <bool kWide, class F>
+__device__ __forceinline__ void for_each_group_row(const HierParams &h, const int32_t *gsrow, F &&f) {
+    if constexpr (!kWide) {
+        for (int g = 0; g < h.G; ++g) {
+            const int32_t gs = gsrow[g];
+            if (gs >= 0 && gs < h.group_rows) f(g, gs);
+        }
+    } else {
+        const int lane = __lane_id();
+        for (int g0 = 0; g0 < h.G; g0 += 64) {
+            const int32_t gs_l = gsrow[min(g0 + lane, h.G - 1)];
+            uint64_t m = __ballot(g0 + lane < h.G && gs_l >= 0 && gs_l < h.group_rows);
+            while (m) {
+                const int b = __builtin_ctzll(m);
+                m &= m - 1;
+                f(g0 + b, __builtin_amdgcn_readlane(gs_l, b));
+            }
+        }
+    }
+}
+
+// Two-level dispatch, stage 1: token t's row, loaded once, to its row in
+// every group it reaches.
+template <int VPT, bool kWide>
+__global__ __launch_bounds__(kCopyThreads) void group_dispatch_kernel(CopyParams c, HierParams h,
+                                                                      const uint16_t *__restrict__ x,
+                                                                      const int32_t *__restrict__ group_slot,
+                                                                      uint16_t *__restrict__ group_buf) {
+    const int t = blockIdx.x;
+    const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x) + static_cast<int64_t>(t) * c.nvec;
+    u32x4 buf[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) buf[v] = __builtin_nontemporal_load(src + min(v0 + v * kCopyThreads, c.nvec - 1));
+    u32x4 *rows = reinterpret_cast<u32x4 *>(group_buf);
+    for_each_group_row<kWide>(h, group_slot + static_cast<int64_t>(t) * h.G, [&](int, int32_t gs) {
+        u32x4 *dst = rows + static_cast<int64_t>(gs) * c.nvec;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int col = v0 + v * kCopyThreads;
+            if (col < c.nvec) dst[col] = buf[v];
+        }
+        if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    });
+}
+
+// Two-level combine, stage 1: for each group the token reaches, the partial
+// sum over the token's entries in that group, rounded to bf16 into the
+// group buffer row group_slot[t,g].  With K <= KG the K rows are loaded once
+// and each group folds its own entries from registers (ascending j, as in
+// gather_fold); gathering per group instead kept half as many loads in
+// flight and loaded row 0 for the other groups' entries: 18 µs slower on a
+// 4096-token step with four groups, 22 µs on 16384 tokens with two.
+template <int KG, bool kWide>
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
+    CopyParams c, HierParams h, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
+    const float *__restrict__ w, const int32_t *__restrict__ group_slot,
+    uint16_t *__restrict__ group_buf) {
+    const int t = blockIdx.x;
+    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
+    const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
+    const int col = blockIdx.y * blockDim.x + threadIdx.x;
+    const int colc = min(col, c.nvec - 1);
+    const int32_t *gsrow = group_slot + static_cast<int64_t>(t) * h.G;
+    u32x4 *rows = reinterpret_cast<u32x4 *>(group_buf);
+    if (c.K <= KG) {
+        // all K rows in flight once, then folded group by group from registers
+        u32x4 in[KG];
+        int32_t grp[KG];
+        float wj[KG];
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+            const int j = min(jj, c.K - 1);
+            const int32_t s = srow[j];
+            const bool ok = jj < c.K && slot_ok(s, c.num_rows);
+            grp[jj] = ok ? (s / h.S) / h.ranks_per_group : -1;
+            wj[jj] = wrow ? wrow[j] : 1.0f;
+            const int64_t row = ok ? s : 0;
+            in[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + row * c.H) + colc);
+        }
+        for_each_group_row<kWide>(h, gsrow, [&](int g, int32_t gs) {
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = __builtin_fmaf(wj[jj], bf16_lo(in[jj][q]), acc[2 * q]);
+                    const float hi = __builtin_fmaf(wj[jj], bf16_hi(in[jj][q]), acc[2 * q + 1]);
+                    acc[2 * q] = grp[jj] == g ? lo : acc[2 * q];
+                    acc[2 * q + 1] = grp[jj] == g ? hi : acc[2 * q + 1];
+                }
+            }
+            if (col < c.nvec) rows[static_cast<int64_t>(gs) * c.nvec + col] = pack_row(acc);
+        });
+        return;
+    }
+    for_each_group_row<kWide>(h, gsrow, [&](int g, int32_t gs) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        gather_fold<KG>(c, y, srow, wrow, colc, GroupOf{h.S, h.ranks_per_group, g}, acc);
+        if (col < c.nvec) rows[static_cast<int64_t>(gs) * c.nvec + col] = pack_row(acc);
+    });
+}
+
+// Two-level combine, stage 2: out[t] = the sum of token t's group rows in
+// ascending g, fp32 accumulate, one rounding to bf16.  Rows are gathered KG
+// at a time, all in flight; a position without a valid row loads row 0 (in
+// bounds) and discards it by a select, as gather_fold does.  With few groups
+// every group is a position; with many (kWide) only the valid rows are,
+// found 64 groups at a time by a ballot.
+template <int KG, bool kWide>
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_groups_kernel(
+    CopyParams c, HierParams h, const uint16_t *__restrict__ group_buf, const int32_t *__restrict__ group_slot,
+    uint16_t *__restrict__ out) {
+    const int t = blockIdx.x;
+    const int col = blockIdx.y * blockDim.x + threadIdx.x;
+    const int colc = min(col, c.nvec - 1);
+    const int32_t *gsrow = group_slot + static_cast<int64_t>(t) * h.G;
+    const u32x4 *rows = reinterpret_cast<const u32x4 *>(group_buf);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    auto fold = [&](const u32x4 (&in)[KG], const bool (&ok)[KG]) {
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = __builtin_fmaf(1.0f, bf16_lo(in[jj][q]), acc[2 * q]);
+                const float hi = __builtin_fmaf(1.0f, bf16_hi(in[jj][q]), acc[2 * q + 1]);
+                acc[2 * q] = ok[jj] ? lo : acc[2 * q];
+                acc[2 * q + 1] = ok[jj] ? hi : acc[2 * q + 1];
+            }
+        }
+    };
+    if constexpr (!kWide) {
+        for (int g0 = 0; g0 < h.G; g0 += KG) {
+            u32x4 in[KG];
+            bool ok[KG];
+#pragma unroll
+            for (int jj = 0; jj < KG; ++jj) {
+                const int32_t gs = gsrow[min(g0 + jj, h.G - 1)];
+                ok[jj] = g0 + jj < h.G && gs >= 0 && gs < h.group_rows;
+                const int64_t row = ok[jj] ? gs : 0;
+                in[jj] = __builtin_nontemporal_load(rows + row * c.nvec + colc);
+            }
+            fold(in, ok);
+        }
+    } else {
+        const int lane = __lane_id();
+        for (int g0 = 0; g0 < h.G; g0 += 64) {
+            const int32_t gs_l = gsrow[min(g0 + lane, h.G - 1)];
+            uint64_t m = __ballot(g0 + lane < h.G && gs_l >= 0 && gs_l < h.group_rows);
+            while (m) {
+                u32x4 in[KG];
+                bool ok[KG];
+#pragma unroll
+                for (int jj = 0; jj < KG; ++jj) {
+                    ok[jj] = m != 0;
+                    const int b = ok[jj] ? __builtin_ctzll(m) : 0;
+                    m &= m - 1;
+                    const int64_t row = ok[jj] ? __builtin_amdgcn_readlane(gs_l, b) : 0;
+                    in[jj] = __builtin_nontemporal_load(rows + row * c.nvec + colc);
+                }
+                fold(in, ok);
+            }
+        }
+    }
+    if (col < c.nvec)
+        __builtin_nontemporal_store(pack_row(acc), reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H) + col);
+}
+
+// Two-level dispatch, stage 2: each group row of the token goes to the
+// entries of that group (with the entry's source index and weight).
+template <int VPT, bool kWide>
+__global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, HierParams h,
+                                                              DispatchArgs a,
+                                                              const int32_t *__restrict__ group_slot,
+                                                              const uint16_t *__restrict__ group_buf) {
+    const int t = blockIdx.x;
+    u32x4 *recv = static_cast<u32x4 *>(a.recv);
+    const int v0 = blockIdx.y * (kCopyThreads * VPT) + threadIdx.x;
+    const int32_t lane_slot = a.slot[static_cast<int64_t>(t) * c.K + min(static_cast<int>(__lane_id()), c.K - 1)];
+    if (blockIdx.y == 0 && static_cast<int>(threadIdx.x) < c.K) {
+        const int j = threadIdx.x;  // lane j of wave 0
+        if (slot_ok(lane_slot, c.num_rows)) {
+            if (a.recv_src) a.recv_src[lane_slot] = t;
+            if (a.recv_w) a.recv_w[lane_slot] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+        }
+    }
+    for_each_group_row<kWide>(h, group_slot + static_cast<int64_t>(t) * h.G, [&](int g, int32_t gs) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(group_buf) + static_cast<int64_t>(gs) * c.nvec;
+        u32x4 buf[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) buf[v] = src[min(v0 + v * kCopyThreads, c.nvec - 1)];
+        const GroupOf in_group{h.S, h.ranks_per_group, g};
+        for (int j = 0; j < c.K; ++j) {
+            const int32_t s = slot_of(lane_slot, j);
+            if (!slot_ok(s, c.num_rows) || !in_group(s)) continue;
+            u32x4 *dst = recv + static_cast<int64_t>(s) * c.nvec;
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                const int col = v0 + v * kCopyThreads;
+                if (col < c.nvec) dst[col] = buf[v];
+            }
+        }
+    });
+}
+
+}  // namespace
+
+hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
+                               int32_t *group_slot, hipStream_t stream) {
+    if (h.ranks_per_group % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0)
+        launch_group_layout_nt<true>(T, R, h, map, group_slot, stream);
+    else
+        launch_group_layout_nt<false>(T, R, h, map, group_slot, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_expand(const CopyParams &c, const HierParams &h, const DispatchArgs &a,
+                         const int32_t *group_slot, const uint16_t *group_buf, hipStream_t stream) {
+    int32_t splits, vpt;
+    copy_grid(c.T, c.nvec, kCopyThreads, &splits, &vpt);
+    CopyParams p = c;
+    p.vpt = vpt;
+    dim3 grid(c.T, splits);
+    switch (vpt) {
+#define EP_EXPAND_CASE(V)                                                                    \
+    case V:                                                                                  \
+        if (h.G > kNarrowGroups)                                                             \
+            expand_kernel<V, true><<<grid, kCopyThreads, 0, stream>>>(p, h, a, group_slot, group_buf); \
+        else                                                                                 \
+            expand_kernel<V, false><<<grid, kCopyThreads, 0, stream>>>(p, h, a, group_slot, group_buf); \
+        break;
+        EP_EXPAND_CASE(1)
+        EP_EXPAND_CASE(2)
+        EP_EXPAND_CASE(3)
+        EP_EXPAND_CASE(4)
+        EP_EXPAND_CASE(5)
+        EP_EXPAND_CASE(6)
+        EP_EXPAND_CASE(7)
+        EP_EXPAND_CASE(8)
+#undef EP_EXPAND_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_group_dispatch(const CopyParams &c, const HierParams &h, const uint16_t *x,
+                                 const int32_t *group_slot, uint16_t *group_buf, hipStream_t stream) {
+    int32_t splits, vpt;
+    copy_grid(c.T, c.nvec, kCopyThreads, &splits, &vpt);
+    CopyParams p = c;
+    p.vpt = vpt;
+    dim3 grid(c.T, splits);
+    switch (vpt) {
+#define EP_GROUP_DISPATCH_CASE(V)                                                                 \
+    case V:                                                                                       \
+        if (h.G > kNarrowGroups)                                                                  \
+            group_dispatch_kernel<V, true><<<grid, kCopyThreads, 0, stream>>>(p, h, x, group_slot, group_buf); \
+        else                                                                                      \
+            group_dispatch_kernel<V, false><<<grid, kCopyThreads, 0, stream>>>(p, h, x, group_slot, group_buf); \
+        break;
+        EP_GROUP_DISPATCH_CASE(1)
+        EP_GROUP_DISPATCH_CASE(2)
+        EP_GROUP_DISPATCH_CASE(3)
+        EP_GROUP_DISPATCH_CASE(4)
+        EP_GROUP_DISPATCH_CASE(5)
+        EP_GROUP_DISPATCH_CASE(6)
+        EP_GROUP_DISPATCH_CASE(7)
+        EP_GROUP_DISPATCH_CASE(8)
+#undef EP_GROUP_DISPATCH_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_groups(const CopyParams &c, const HierParams &h, const uint16_t *group_buf,
+                                 const int32_t *group_slot, uint16_t *out, hipStream_t stream) {
+    int32_t splits, threads;
+    combine_grid(c.T, c.nvec, &splits, &threads);
+    dim3 grid(c.T, splits);
+    // rows in flight per round: all G positions with few groups; with many,
+    // the valid rows, of which a token has at most min(G, K)
+    const bool wide = h.G > kNarrowGroups;
+    const int n = wide ? (h.G < c.K ? h.G : c.K) : h.G;
+#define EP_COMBINE_GROUPS(KG)                                                                          \
+    do {                                                                                               \
+        if (wide)                                                                                      \
+            combine_groups_kernel<KG, true><<<grid, threads, 0, stream>>>(c, h, group_buf, group_slot, out); \
+        else                                                                                           \
+            combine_groups_kernel<KG, false><<<grid, threads, 0, stream>>>(c, h, group_buf, group_slot, out); \
+    } while (0)
+    if (n <= 2)
+        EP_COMBINE_GROUPS(2);
+    else if (n <= 4)
+        EP_COMBINE_GROUPS(4);
+    else
+        EP_COMBINE_GROUPS(8);
+#undef EP_COMBINE_GROUPS
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, const uint16_t *y,
+                                  const int32_t *slot, const float *w, const int32_t *group_slot,
+                                  uint16_t *group_buf, hipStream_t stream) {
+    int32_t splits, threads;
+    combine_grid(c.T, c.nvec, &splits, &threads);
+    dim3 grid(c.T, splits);
+    const bool wide = h.G > kNarrowGroups;
+    if (c.K <= 4 && wide) {
+        combine_partial_kernel<4, true><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
+    } else if (c.K <= 4) {
+        combine_partial_kernel<4, false><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
+    } else if (wide) {
+        combine_partial_kernel<8, true><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
+    } else {
+        combine_partial_kernel<8, false><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace epget
