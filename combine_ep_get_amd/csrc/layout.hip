@@ -191,26 +191,41 @@ __device__ void token_pass(const LayoutParams &p, int t0, int t1, const int *s_i
         }
         return;
     }
-    const int nr = ntok * p.R;
-    for (int i = threadIdx.x; i < nr; i += NT) {
-        const int tl = p.div_R(i), r = i - tl * p.R;
-        const int *ids = s_idx + tl * p.K;
-        int in = 0;
-        for (int j = 0; j < p.K; ++j) in |= (ids[j] >> kRankShift) == r;
-        map[i] = static_cast<uint8_t>(in);
-        if (in) atomicAdd(&s_hist[p.E + r], 1);
-    }
-    const int ng = ntok * p.G;
-    for (int i = threadIdx.x; i < ng; i += NT) {
-        const int tl = p.div_G(i), g = i - tl * p.G;
-        const int lo = g * p.ranks_per_group, hi = lo + p.ranks_per_group;
-        const int *ids = s_idx + tl * p.K;
-        int in = 0;
-        for (int j = 0; j < p.K; ++j) {
-            const int r = ids[j] >> kRankShift;
-            in |= r >= lo && r < hi;
+    // R > 64.  Map rows: the chunk's rows (one run of ntok * R bytes) are
+    // cleared with 16-byte stores, then each entry sets its rank's byte
+    // (entries of a token that share a rank write the same 1).  The clearing
+    // stores are waited for before the barrier, so no 1 can be overtaken by
+    // the 0 it replaces.
+    const int nbytes = ntok * p.R;
+    const int head = min(static_cast<int>((16 - (reinterpret_cast<uintptr_t>(map) & 15)) & 15), nbytes);
+    const int nunits = (nbytes - head) >> 4;
+    const int tail0 = head + (nunits << 4);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int u = threadIdx.x; u < nunits; u += NT) *reinterpret_cast<u32x4 *>(map + head + (u << 4)) = zero;
+    for (int i = threadIdx.x; i < head + (nbytes - tail0); i += NT) map[i < head ? i : tail0 + (i - head)] = 0;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    // An entry also counts its token for its rank (its group) when no
+    // earlier entry of the token has that rank (group).
+    const int nent = ntok * p.K;
+    for (int i = threadIdx.x; i < nent; i += NT) {
+        const int v = s_idx[i];
+        if (v < 0) continue;
+        const int tl = i / p.K, j = i - tl * p.K;
+        const int *ids = s_idx + (i - j);
+        const int r = v >> kRankShift;
+        const int g = r / p.ranks_per_group;
+        map[static_cast<int64_t>(tl) * p.R + r] = 1;
+        bool first_r = true, first_g = true;
+        for (int jj = 0; jj < j; ++jj) {
+            const int u = ids[jj];
+            if (u < 0) continue;
+            const int ru = u >> kRankShift;
+            first_r &= ru != r;
+            first_g &= ru / p.ranks_per_group != g;
         }
-        if (in) atomicAdd(&s_hist[p.E + p.R + g], 1);
+        if (first_r) atomicAdd(&s_hist[p.E + r], 1);
+        if (first_g) atomicAdd(&s_hist[p.E + p.R + g], 1);
     }
 }
 

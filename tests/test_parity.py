@@ -298,6 +298,42 @@ def test_large_expert_count_and_rank_count(ep):
     _case(ep, _route_uniform(rng, T, E, K), E, R, H=16)
 
 
+@pytest.mark.parametrize("T,E,R,G,K", [
+    (100, 130, 65, 5, 6),      # one chunk; rows of 65 bytes: unaligned row starts
+    (2500, 200, 100, 4, 6),    # count + table sums (15 chunks)
+    (9000, 2048, 1024, 8, 3),  # count + scan (27 chunks of 341 tokens, 8 experts per thread)
+    (300, 2048, 1024, 1024, 8),  # three chunks: the one call runs as a single kernel
+])
+def test_many_ranks_map_and_unique_counts(ep, T, E, R, G, K):
+    """More than 64 ranks: the chunk's map rows are cleared, then each entry
+    sets its rank's byte; unique tokens per rank and group count a token's
+    first entry on each.  Empty entries and two entries of one token on the
+    same rank occur."""
+    print(f"[parity] many ranks T={T} E={E} R={R} G={G} K={K}", flush=True)
+    rng = np.random.default_rng(T + R)
+    idx = _route_uniform(rng, T, E, K)
+    L = E // R
+    same_rank = rng.random(T) < 0.3           # second entry on the first entry's rank
+    idx[same_rank, 1] = (idx[same_rank, 0] // L) * L + (idx[same_rank, 0] + 1) % L
+    dup = idx[same_rank, 1] == idx[same_rank, 0]
+    idx[np.flatnonzero(same_rank)[dup], 1] = -1
+    idx[rng.random(idx.shape) < 0.05] = -1
+    H = 64
+    counts = np.bincount(idx[idx >= 0].ravel(), minlength=E)
+    S = tight_stride(counts, E, R) + 5
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    ref, _, _ = run_full(ep, idx, w, x, E, R, G, 1, S)
+    # the one-call layout and dispatch leaves the same layout and rows
+    p = ep.Problem.make(T, H, E, K, R, G, 1, S)
+    bufs = ep.alloc_layout(p)
+    recv = torch.empty((R * S, H), dtype=torch.int16, device="cuda")
+    ep.ep_layout_dispatch(p, dev(idx), *bufs.args(), None, bf16_dev(x), dev(w), recv, None, None)
+    assert_layout_matches(ep, bufs, ep.ep_read_status(bufs.workspace), ref)
+    sl = ref.token_slot[ref.token_slot >= 0]
+    assert_same(host_u16(recv)[sl], oracle.dispatch(x, ref.token_slot, R * S, w)[0][sl])
+
+
 def test_cumulative_expert_counts_and_cached_layout(ep):
     """Cumulative per-expert receive counts across calls, and dispatch/combine
     reusing one layout (cached mode) for new activations."""
