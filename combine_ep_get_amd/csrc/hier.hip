@@ -101,15 +101,112 @@ __global__ __launch_bounds__(NT) void group_layout_kernel(int32_t T, int32_t R, 
     }
 }
 
+// Group slots of a batch of more than 4096 tokens: tiles of kTileTokens
+// tokens, one workgroup per (tile, group), all running at once.  A
+// workgroup counts the tokens of the earlier tiles that reach its group
+// (reading their rank bytes again, four tokens per thread in flight, together
+// with its own tile's), then places its own tile as one pass of
+// group_layout_kernel does (two flags per thread).  The recount costs each workgroup one read of the earlier part of
+// the map, which stays in cache; a single workgroup per group walked the
+// batch pass after pass, each pass paying the map's load latency on one CU.
+constexpr int kTileThreads = 1024;
+constexpr int kTileTpt = 2;
+constexpr int kRecountTpt = 4;
+constexpr int kTileTokens = kTileThreads * kTileTpt;
+
+template <bool kWords>
+__global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, int32_t R, HierParams h,
+                                                                   const uint8_t *__restrict__ map,
+                                                                   int32_t *__restrict__ group_slot) {
+    __shared__ uint8_t s_flag[kTileTokens];
+    __shared__ int s_first[kTileThreads];
+    __shared__ uint32_t s_bits[kTileThreads];
+    __shared__ int s_wsum[kTileThreads / 64];
+    const int c = blockIdx.x, g = blockIdx.y;
+    const int i = threadIdx.x, lane = __lane_id(), w = i >> 6;
+    const int r0 = g * h.ranks_per_group;
+    const int base = c * kTileTokens;
+    // the tile's own rank bytes first, so that their loads are in flight
+    // with the recount's
+    uint32_t in_tile[kTileTpt];
+#pragma unroll
+    for (int k = 0; k < kTileTpt; ++k) in_tile[k] = 0;
+    for (int r = 0; r < h.ranks_per_group; r += kWords ? 4 : 1) {
+#pragma unroll
+        for (int k = 0; k < kTileTpt; ++k) {
+            const int t = min(base + i + k * kTileThreads, T - 1);
+            const uint8_t *b = map + static_cast<int64_t>(t) * R + r0 + r;
+            in_tile[k] |= kWords ? *reinterpret_cast<const uint32_t *>(b) : *b;
+        }
+    }
+    // 1. tokens before the tile that reach the group, kRecountTpt per thread
+    // in flight
+    int cnt = 0;
+    for (int t0 = i; t0 < base; t0 += kRecountTpt * kTileThreads) {
+        uint32_t in[kRecountTpt];
+#pragma unroll
+        for (int k = 0; k < kRecountTpt; ++k) in[k] = 0;
+        for (int r = 0; r < h.ranks_per_group; r += kWords ? 4 : 1) {
+#pragma unroll
+            for (int k = 0; k < kRecountTpt; ++k) {
+                if (t0 - i + k * kTileThreads >= base) break;
+                const int t = min(t0 + k * kTileThreads, base - 1);
+                const uint8_t *b = map + static_cast<int64_t>(t) * R + r0 + r;
+                in[k] |= kWords ? *reinterpret_cast<const uint32_t *>(b) : *b;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kRecountTpt; ++k) cnt += (t0 + k * kTileThreads < base && in[k]) ? 1 : 0;
+    }
+    const int cnt_incl = wave_inclusive_sum(cnt);
+    if (lane == 63) s_wsum[w] = cnt_incl;
+    // 2. the tile: flags in token order, kTileTpt consecutive flags per thread
+#pragma unroll
+    for (int k = 0; k < kTileTpt; ++k)
+        s_flag[i + k * kTileThreads] = (base + i + k * kTileThreads < T && in_tile[k]) ? 1 : 0;
+    __syncthreads();
+    int carry = 0;
+#pragma unroll
+    for (int q = 0; q < kTileThreads / 64; ++q) carry += s_wsum[q];
+    __syncthreads();
+    uint32_t bits = 0;
+#pragma unroll
+    for (int q = 0; q < kTileTpt; ++q) bits |= static_cast<uint32_t>(s_flag[i * kTileTpt + q]) << q;
+    const int n = __popc(bits);
+    const int incl = wave_inclusive_sum(n);
+    if (lane == 63) s_wsum[w] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int q = 0; q < kTileThreads / 64; ++q) before += q < w ? s_wsum[q] : 0;
+    s_first[i] = carry + before + incl - n;
+    s_bits[i] = bits;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTileTpt; ++k) {
+        const int e = i + k * kTileThreads;  // token base + e, owned by thread e / kTileTpt
+        const int t = base + e;
+        if (t < T) {
+            const uint32_t ob = s_bits[e / kTileTpt];
+            const int b = e % kTileTpt;
+            const int pos = s_first[e / kTileTpt] + __popc(ob & ((1u << b) - 1u));
+            group_slot[static_cast<int64_t>(t) * h.G + g] =
+                ((ob >> b) & 1u) && pos < h.SG ? g * h.SG + pos : -1;
+        }
+    }
+}
+
 template <bool kWords>
 void launch_group_layout_nt(int32_t T, int32_t R, const HierParams &h, const uint8_t *map, int32_t *group_slot,
                             hipStream_t stream) {
-    if (T <= 64 * kGroupTpt)
+    if (T <= 64 * kGroupTpt) {
         group_layout_kernel<kWords, 64><<<h.G, 64, 0, stream>>>(T, R, h, map, group_slot);
-    else if (T <= 256 * kGroupTpt)
+    } else if (T <= 256 * kGroupTpt) {
         group_layout_kernel<kWords, 256><<<h.G, 256, 0, stream>>>(T, R, h, map, group_slot);
-    else
-        group_layout_kernel<kWords, 1024><<<h.G, 1024, 0, stream>>>(T, R, h, map, group_slot);
+    } else {
+        const dim3 grid((T + kTileTokens - 1) / kTileTokens, h.G);
+        group_tiles_kernel<kWords><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot);
+    }
 }
 
 // Group of a valid entry slot in the two-level path: rank = slot / S,
