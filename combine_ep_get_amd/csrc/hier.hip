@@ -17,15 +17,16 @@
 namespace epget {
 namespace {
 
-// Group slots.  One workgroup of NT threads per group takes the tokens in
-// passes of NT * kGroupTpt.  In a pass, thread i first reads the rank bytes
-// of tokens i, i + NT, i + 2 NT, ... (neighbouring lanes read neighbouring
-// rows) and leaves a 0/1 flag per token in LDS; it then owns kGroupTpt
-// consecutive flags, counts them, and a workgroup scan (DPP inside waves,
-// wave totals through LDS) gives each thread its first position; the slots
-// are written back in the first order, so the stores of a wave also cover
-// neighbouring rows.  The launch picks the smallest NT whose pass holds the
-// batch (up to 16384 tokens), so a batch pays its load latency once.
+// Group slots of a batch of up to 4096 tokens.  One workgroup of NT threads
+// per group takes the tokens in passes of NT * kGroupTpt.  In a pass, thread
+// i first reads the rank bytes of tokens i, i + NT, i + 2 NT, ...
+// (neighbouring lanes read neighbouring rows) and leaves a 0/1 flag per
+// token in LDS; it then owns kGroupTpt consecutive flags, counts them, and a
+// workgroup scan (DPP inside waves, wave totals through LDS) gives each
+// thread its first position; the slots are written back in the first order,
+// so the stores of a wave also cover neighbouring rows.  The launch picks the
+// smallest NT whose pass holds the batch, so the batch is one pass and pays
+// its load latency once.
 constexpr int kGroupTpt = 16;  // flags per thread in the scan
 
 // kWords: the group's rank bytes are read four at a time (ranks per group a
