@@ -437,6 +437,14 @@ def main():
     ceiling = copy_probe(torch)
 
     nbytes = algorithmic_bytes(wl, fp8=args.fp8)
+    if args.hier:
+        # the two-level path also writes each (token, group) row into the
+        # group buffer and reads it back, once in dispatch and once in
+        # combine; its dispatch phase also derives the group slots (reads the
+        # rank map, writes [T,G] slots)
+        group_rows = int(bufs.group_token_count.sum().item())
+        nbytes["dispatch"] += wl.T * wl.R + 4 * wl.T * G + 2 * group_rows * wl.H * 2
+        nbytes["combine"] += 2 * group_rows * wl.H * 2
     total_bytes = sum(nbytes.values())
     eff_gbps = total_bytes / (ms_step * 1e-3) / 1e9
     if fused:
@@ -468,7 +476,7 @@ def main():
         "dtype": "fp8-e4m3 dispatch, bf16 combine" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "R": wl.R,
-                   "G": wl.G, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
+                   "G": p.num_groups, "A": wl.A, "S": S, "routing": wl.routing, "seed": wl.seed,
                    "dispatch": "fp8" if args.fp8 else "bf16",
                    "path": "two-level (group buffer)" if args.hier else "flat",
                    "layout_dispatch": ("one call (ep_layout_dispatch_fp8)" if args.fp8 else
