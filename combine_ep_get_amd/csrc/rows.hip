@@ -155,6 +155,51 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
         __builtin_nontemporal_store(pack_row(acc), reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H) + col);
 }
 
+// Rows of fewer than kNarrowVectors 16-byte vectors (under 1 KB): one
+// thread per (entry, vector) for the dispatch and one per (token, vector)
+// for the combine, so that a workgroup spans several tokens instead of
+// leaving most of its lanes idle (at 16-byte rows a token-per-workgroup
+// dispatch kept one lane of 128 busy).
+constexpr int kNarrowVectors = 64;
+constexpr int kNarrowThreads = 256;
+
+__global__ __launch_bounds__(kNarrowThreads) void dispatch_narrow_kernel(CopyParams c, DispatchArgs a) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * kNarrowThreads + threadIdx.x;
+    if (gid >= static_cast<int64_t>(c.T) * c.K * c.nvec) return;
+    const int64_t e = gid / c.nvec;  // entry (t, j) = t * K + j
+    const int v = static_cast<int>(gid - e * c.nvec);
+    const int t = static_cast<int>(e / c.K);
+    const int32_t s = a.slot[e];
+    if (!slot_ok(s, c.num_rows)) return;
+    // x[t] is read by its K entries, so its loads stay cached
+    const u32x4 *src = static_cast<const u32x4 *>(a.x) + static_cast<int64_t>(t) * c.nvec;
+    static_cast<u32x4 *>(a.recv)[static_cast<int64_t>(s) * c.nvec + v] = src[v];
+    if (v == 0) {
+        if (a.recv_src) a.recv_src[s] = t;
+        if (a.recv_w) a.recv_w[s] = a.w ? a.w[e] : 1.0f;
+    }
+    if (a.x_sf && v < a.nsf) a.recv_sf[s * a.sf_ts + v * a.sf_hs] = a.x_sf[static_cast<int64_t>(t) * a.nsf + v];
+}
+
+template <int KG>
+__global__ __launch_bounds__(kNarrowThreads) void combine_narrow_kernel(
+    CopyParams c, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
+    const float *__restrict__ w, uint16_t *__restrict__ out) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * kNarrowThreads + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(c.T) * c.nvec;
+    const int64_t gc = gid < total ? gid : total - 1;
+    const int t = static_cast<int>(gc / c.nvec);
+    const int col = static_cast<int>(gc - static_cast<int64_t>(t) * c.nvec);
+    const int32_t *srow = slot + static_cast<int64_t>(t) * c.K;
+    const float *wrow = w ? w + static_cast<int64_t>(t) * c.K : nullptr;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    gather_fold<KG>(c, y, srow, wrow, col, KeepAll{}, acc);
+    if (gid < total)
+        __builtin_nontemporal_store(pack_row(acc), reinterpret_cast<u32x4 *>(out + static_cast<int64_t>(t) * c.H) + col);
+}
+
 // combined_topk_weights: one thread per (token, top-k) entry.
 __global__ __launch_bounds__(256) void combine_weights_kernel(CopyParams c, const float *__restrict__ recv_w,
                                                               const int32_t *__restrict__ slot,
@@ -196,6 +241,13 @@ void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads) {
 }
 
 hipError_t launch_dispatch(const CopyParams &c, const DispatchArgs &a, hipStream_t stream) {
+    if (c.nvec < kNarrowVectors) {
+        const int64_t n = static_cast<int64_t>(c.T) * c.K * c.nvec;
+        const int64_t blocks = (n + kNarrowThreads - 1) / kNarrowThreads;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        dispatch_narrow_kernel<<<static_cast<uint32_t>(blocks), kNarrowThreads, 0, stream>>>(c, a);
+        return hipGetLastError();
+    }
     // batches so small that rows split into one-vector pieces take the
     // wider workgroups of the single-kernel layout + dispatch (decode-sized
     // dispatch 0.4 µs faster; at two or more vectors per thread they were
@@ -240,6 +292,21 @@ hipError_t launch_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t 
 
 hipError_t launch_combine(const CopyParams &c, const uint16_t *y, const int32_t *slot,
                           const float *w, uint16_t *out, hipStream_t stream) {
+    if (c.nvec < kNarrowVectors) {
+        const int64_t n = static_cast<int64_t>(c.T) * c.nvec;
+        const int64_t blocks = (n + kNarrowThreads - 1) / kNarrowThreads;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        const uint32_t g = static_cast<uint32_t>(blocks);
+        if (c.K <= 1)
+            combine_narrow_kernel<1><<<g, kNarrowThreads, 0, stream>>>(c, y, slot, w, out);
+        else if (c.K <= 2)
+            combine_narrow_kernel<2><<<g, kNarrowThreads, 0, stream>>>(c, y, slot, w, out);
+        else if (c.K <= 4)
+            combine_narrow_kernel<4><<<g, kNarrowThreads, 0, stream>>>(c, y, slot, w, out);
+        else
+            combine_narrow_kernel<8><<<g, kNarrowThreads, 0, stream>>>(c, y, slot, w, out);
+        return hipGetLastError();
+    }
     int32_t splits, threads;
     combine_grid(c.T, c.nvec, &splits, &threads);
     dim3 grid(c.T, splits);
