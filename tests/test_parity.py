@@ -334,6 +334,18 @@ def test_many_ranks_map_and_unique_counts(ep, T, E, R, G, K):
     assert_same(host_u16(recv)[sl], oracle.dispatch(x, ref.token_slot, R * S, w)[0][sl])
 
 
+@pytest.mark.parametrize("T,H,K", [(3001, 8, 3), (5000, 64, 8), (777, 504, 6), (900, 512, 4)])
+def test_narrow_rows(ep, T, H, K):
+    """Rows under 1 KB take one thread per (entry, vector) in dispatch and per
+    (token, vector) in combine: one-vector rows, a ragged last workgroup, 63
+    vectors, and 64 (the first width back on the per-token kernels)."""
+    print(f"[parity] narrow rows T={T} H={H} K={K}", flush=True)
+    rng = np.random.default_rng(T + H)
+    idx = _route_uniform(rng, T, 64, K)
+    idx[rng.random(idx.shape) < 0.05] = -1
+    _case(ep, idx, 64, 8, H=H, seed=T)
+
+
 def test_cumulative_expert_counts_and_cached_layout(ep):
     """Cumulative per-expert receive counts across calls, and dispatch/combine
     reusing one layout (cached mode) for new activations."""
