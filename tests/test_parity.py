@@ -334,11 +334,13 @@ def test_many_ranks_map_and_unique_counts(ep, T, E, R, G, K):
     assert_same(host_u16(recv)[sl], oracle.dispatch(x, ref.token_slot, R * S, w)[0][sl])
 
 
-@pytest.mark.parametrize("T,H,K", [(3001, 8, 3), (5000, 64, 8), (777, 504, 6), (900, 512, 4)])
+@pytest.mark.parametrize("T,H,K", [(20001, 8, 4), (5000, 64, 8), (17000, 504, 6), (3001, 8, 3), (900, 512, 4)])
 def test_narrow_rows(ep, T, H, K):
     """Rows under 1 KB take one thread per (entry, vector) in dispatch and per
-    (token, vector) in combine: one-vector rows, a ragged last workgroup, 63
-    vectors, and 64 (the first width back on the per-token kernels)."""
+    (token, vector) in combine once the batch fills the chip that way:
+    one-vector rows with a ragged last workgroup, 8 and 63 vectors; a small
+    batch of one-vector rows that stays on the per-token kernels; and 64
+    vectors, the first width that always does."""
     print(f"[parity] narrow rows T={T} H={H} K={K}", flush=True)
     rng = np.random.default_rng(T + H)
     idx = _route_uniform(rng, T, 64, K)
