@@ -1055,7 +1055,13 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
                                   hipStream_t stream) {
     // the single-kernel form has larger workgroups: its slot derivation is
     // on the critical path, and 256 threads share it faster than 128
-    const bool one_chunk = p.T > 0 && static_cast<int64_t>(p.T) * p.K <= kFusedMaxEntries;
+    // Past 64 ranks one workgroup builds the rank map of the single-kernel
+    // form chunk by chunk, and at four chunks that outlasts the dispatch: the
+    // count pass plus one kernel took 25.2 µs against 32.7 µs (T = 512,
+    // E = 1024, R = 128), while at two or three chunks the single kernel
+    // stays ahead (16.4 against 26.8 µs at T = 200, R = 256).
+    const bool one_chunk = p.T > 0 && static_cast<int64_t>(p.T) * p.K <= kFusedMaxEntries &&
+                           (p.nchunks <= 3 || p.R <= 64);
     int32_t splits, vpt;
     copy_grid(c.T, c.nvec, one_chunk ? kFusedThreads : kCopyThreads, &splits, &vpt);
     CopyParams cp = c;

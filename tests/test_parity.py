@@ -303,6 +303,7 @@ def test_large_expert_count_and_rank_count(ep):
     (2500, 200, 100, 4, 6),    # count + table sums (15 chunks)
     (9000, 2048, 1024, 8, 3),  # count + scan (27 chunks of 341 tokens, 8 experts per thread)
     (300, 2048, 1024, 1024, 8),  # three chunks: the one call runs as a single kernel
+    (512, 1024, 128, 8, 8),      # four chunks: the one call runs the count pass and one kernel
 ])
 def test_many_ranks_map_and_unique_counts(ep, T, E, R, G, K):
     """More than 64 ranks: the chunk's map rows are cleared, then each entry
