@@ -169,9 +169,10 @@ int ep_dispatch(const ep_problem *problem, const uint16_t *x,
  * status of both.  [SYM] §6.1 feeds the layout's prefix sums and slots
  * straight into the dispatch launch; here, when the batch is small enough
  * for four layout chunks of 1024 entries (T*K <= 4096 after rounding to
- * whole tokens: decode-sized batches), both run as a single kernel in which
- * every dispatching workgroup derives its own token's slots, which saves a
- * launch on the latency-bound path.  Batches of up to 128 chunks with
+ * whole tokens: decode-sized batches; three chunks when R > 64), both run
+ * as a single kernel in which every dispatching workgroup derives its own
+ * token's slots, which saves a launch on the latency-bound path.  Batches of
+ * up to 128 chunks with
  * expert_alignment 1 run the count pass and then one kernel that finishes
  * the layout while each dispatching workgroup derives its token's slots from
  * per-chunk counts (two launches instead of three); other batches run the
