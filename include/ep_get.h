@@ -172,11 +172,10 @@ int ep_dispatch(const ep_problem *problem, const uint16_t *x,
  * whole tokens: decode-sized batches; three chunks when R > 64), both run
  * as a single kernel in which every dispatching workgroup derives its own
  * token's slots, which saves a launch on the latency-bound path.  Batches of
- * up to 128 chunks with
- * expert_alignment 1 run the count pass and then one kernel that finishes
- * the layout while each dispatching workgroup derives its token's slots from
- * per-chunk counts (two launches instead of three); other batches run the
- * two calls' kernels.
+ * up to 128 chunks with expert_alignment 1 run the count pass and then one
+ * kernel that finishes the layout while each dispatching workgroup derives
+ * its token's slots from per-chunk counts (two launches instead of three);
+ * other batches run the two calls' kernels.
  * token_slot is written as ep_get_layout writes it. */
 int ep_layout_dispatch(const ep_problem *problem, const int32_t *topk_idx,
                        int32_t *expert_count, int32_t *expert_offset,
