@@ -144,6 +144,44 @@ def test_dispatch_fp8_parity(ep, name, column_major):
     assert_same(g_w.cpu().numpy()[s], rw[s])
 
 
+@pytest.mark.parametrize("H,column_major", [(256, False), (256, True), (896, True)])
+def test_dispatch_fp8_narrow_rows(ep, H, column_major):
+    """FP8 rows under 1 KB with enough entries to take the packed dispatch (one
+    thread per (entry, 16-byte vector), the scales placed by the first H/128
+    vectors' threads), in both scale layouts; 896-byte rows are the widest."""
+    print(f"[parity-fp8] narrow rows H={H} column_major={column_major}", flush=True)
+    rng = np.random.default_rng(H + column_major)
+    T, E, R, K = 3000, 64, 8, 6
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.05] = -1
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    counts = np.bincount(idx[idx >= 0].ravel(), minlength=E)
+    S = int((counts.reshape(R, -1).sum(1)).max())
+    rows = R * S
+    lay = oracle.layout(idx, E, R, S, 1)
+    q, sf = oracle.quantize_fp8(x)
+    rq, rsf, (ts, hs), rsrc, rw = oracle.dispatch_fp8(q, sf, lay.token_slot, rows, w,
+                                                     column_major_sf=column_major)
+    p = ep.Problem.make(T, H, E, K, R, 1, 1, S)
+    bufs = ep.alloc_layout(p)
+    ep.ep_get_layout(p, dev(idx), *bufs.args())
+    g_q = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+    g_sf = torch.full((rsf.size,), float("nan"), dtype=torch.float32, device="cuda")
+    g_src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch_fp8(p, dev(q), dev(sf), dev(w), bufs.token_slot, g_q, g_sf, ts, hs, g_src, g_w)
+    torch.cuda.synchronize()
+    s = lay.token_slot.ravel()
+    s = s[s >= 0]
+    assert_same(g_q.cpu().numpy()[s], rq[s])
+    nb = H // 128
+    idx_sf = (s[:, None] * ts + np.arange(nb)[None, :] * hs).ravel()
+    assert_same(g_sf.cpu().numpy()[idx_sf], rsf[idx_sf])
+    assert_same(g_src.cpu().numpy()[s], rsrc[s])
+    assert_same(g_w.cpu().numpy()[s], rw[s])
+
+
 @pytest.mark.parametrize("name,column_major", [("tiny", False), ("decode128", True), ("decode128", False),
                                                ("prefill4k", True)])
 def test_layout_dispatch_fp8_parity(ep, name, column_major):
