@@ -335,7 +335,8 @@ def test_many_ranks_map_and_unique_counts(ep, T, E, R, G, K):
     assert_same(host_u16(recv)[sl], oracle.dispatch(x, ref.token_slot, R * S, w)[0][sl])
 
 
-@pytest.mark.parametrize("T,H,K", [(20001, 8, 4), (5000, 64, 8), (17000, 504, 6), (3001, 8, 3), (900, 512, 4)])
+@pytest.mark.parametrize("T,H,K", [(20001, 8, 4), (5000, 64, 8), (17000, 504, 6), (40000, 8, 1), (20000, 16, 2),
+                                   (3001, 8, 3), (900, 512, 4)])
 def test_narrow_rows(ep, T, H, K):
     """Rows under 1 KB take one thread per (entry, vector) in dispatch and per
     (token, vector) in combine once the batch fills the chip that way:
