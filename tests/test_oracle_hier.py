@@ -5,8 +5,14 @@
 - two-level dispatch must leave exactly the rows the flat dispatch leaves;
 - one-hot weights through the two-level combine return x exactly;
 - weighted two-level combine stays within the bound set by rounding each
-  group partial to bf16, against the flat fp64 combine.
+  group partial to bf16, against the flat fp64 combine;
+- a hand-worked fixture (tests/golden/combine_hier_handworked.json) fixes
+  the bits of the partials and of the output: the fp32 fold, its top-k
+  order, the bf16 rounding of each partial and the exact sum over groups.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -76,7 +82,7 @@ def test_two_level_combine_one_hot_returns_x():
     np.testing.assert_array_equal(oracle.bf16_to_double(out), oracle.bf16_to_double(inp.x))
 
 
-@pytest.mark.parametrize("name,G", [("tiny", 2), ("decode128", 2), ("decode128", 8)])
+@pytest.mark.parametrize("name,G", [("tiny", 1), ("tiny", 2), ("decode128", 2), ("decode128", 8)])
 def test_two_level_combine_within_partial_rounding_bound(name, G):
     inp, wl, S, lay = _setup(name)
     lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, G)
@@ -94,6 +100,34 @@ def test_two_level_combine_within_partial_rounding_bound(name, G):
     # (fp32 folding error is far smaller)
     bound = 2.0 ** -8 * (part + np.abs(flat) + np.abs(got)) + 1e-30
     assert np.all(np.abs(got - flat) <= bound)
-    # G = 1 reduces to a single fp32 partial: equal to the flat fp32 fold
+    # with one group the output is the token's single group row: a bf16
+    # value rounded again to bf16 is unchanged
     if G == 1:
-        np.testing.assert_array_equal(out, oracle.combine(y, lay.token_slot, inp.topk_weights))
+        t = np.nonzero(gs[:, 0] >= 0)[0]
+        np.testing.assert_array_equal(out[t], gbuf[gs[t, 0]])
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "combine_hier_handworked.json")
+
+
+def _golden_case(c):
+    """Arrays of one hand-worked case: y filled with y_other except the
+    named rows."""
+    R, S, H = c["R"], c["S"], c["H"]
+    y = np.full((R * S, H), int(c["y_other"], 16), np.uint16)
+    for row, vals in c["y"].items():
+        y[int(row)] = [int(v, 16) for v in vals]
+    slot = np.array(c["token_slot"], np.int32)
+    gsl = np.array(c["group_slot"], np.int32)
+    w = np.array([[float.fromhex(v) for v in r] for r in c["weights"]], np.float32)
+    return y, slot, gsl, w
+
+
+@pytest.mark.parametrize("case", [c["name"] for c in json.load(open(GOLDEN))["cases"]])
+def test_golden_handworked_two_level_combine(case):
+    c = next(c for c in json.load(open(GOLDEN))["cases"] if c["name"] == case)
+    y, slot, gsl, w = _golden_case(c)
+    gbuf, out = oracle.combine_hier(y, slot, w, gsl, c["R"], c["S"], c["SG"])
+    for row, vals in c["group_rows"].items():
+        assert [int(v) for v in gbuf[int(row)]] == [int(v, 16) for v in vals], (case, "group row", row)
+    assert out.tolist() == [[int(v, 16) for v in r] for r in c["out"]], (case, "out")

@@ -6,6 +6,7 @@ round-to-nearest-even, ...), builds it with gcc into a temporary library and
 runs the pin tests against that build.  At least one pin must fail.  This
 runs on the CPU only.
 """
+import json
 import os
 import subprocess
 
@@ -45,6 +46,24 @@ MUTATIONS = {
     "group_slot_off_by_one": ("group_slot[t * G + g] = pos < SG ? (int32_t)(g * SG + pos) : -1;",
                               "group_slot[t * G + g] = pos < SG ? (int32_t)(g * SG + pos + 1) : -1;"),
     "slot_group_modulo": ("return (int32_t)((s / S) / (R / G));", "return (int32_t)((s / S) % G);"),
+    "partial_folded_in_double": (
+        "float acc = 0.0f;\n                for (int32_t j = 0; j < K; ++j) {",
+        "double acc = 0.0;\n                for (int32_t j = 0; j < K; ++j) {"
+        "\n#define fmaf(a, b, c) fma((double)(a), (double)(b), (c))"),
+    "partial_topk_order_reversed": (
+        "for (int32_t j = 0; j < K; ++j) {\n                    int64_t s = token_slot[t * K + j];\n"
+        "                    if (s < 0 || s >= num_rows || slot_group(s, S, R, G) != g) continue;",
+        "for (int32_t j = K - 1; j >= 0; --j) {\n                    int64_t s = token_slot[t * K + j];\n"
+        "                    if (s < 0 || s >= num_rows || slot_group(s, S, R, G) != g) continue;"),
+    "group_sum_in_float": (
+        "double acc = 0.0;\n            for (int32_t g = 0; g < G; ++g) {",
+        "float acc = 0.0f;\n            for (int32_t g = 0; g < G; ++g) {"),
+    "partials_summed_unrounded": (
+        "acc += (double)bf16_to_float(group_buf[gs * H + h]);",
+        "{ float pa = 0.0f; for (int32_t j = 0; j < K; ++j) { int64_t s = token_slot[t * K + j]; "
+        "if (s < 0 || s >= num_rows || slot_group(s, S, R, G) != g) continue; "
+        "pa = fmaf(topk_weights ? topk_weights[t * K + j] : 1.0f, bf16_to_float(y[s * H + h]), pa); } "
+        "acc += (double)pa; }"),
     "fp8_scale_strides_swapped": ("recv_sf[s * sf_token_stride + b * sf_hidden_stride]",
                                   "recv_sf[s * sf_hidden_stride + b * sf_token_stride]"),
 }
@@ -71,6 +90,8 @@ def _pin_suite():
     hierpins.test_group_slots("prefill4k", 2)
     hierpins.test_two_level_dispatch_equals_flat("tiny")
     hierpins.test_two_level_combine_one_hot_returns_x()
+    for c in json.load(open(hierpins.GOLDEN))["cases"]:
+        hierpins.test_golden_handworked_two_level_combine(c["name"])
     # token-major scales: a planted stride mistake then stays inside the buffer
     fp8pins.test_dispatch_fp8_moves_codes_and_scales(False)
 
