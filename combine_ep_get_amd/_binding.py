@@ -94,7 +94,7 @@ def load():
         lib.ep_layout_dispatch_fp8.restype = ctypes.c_int
         lib.ep_layout_dispatch_fp8.argtypes = [P] + [vp] * 10 + [sz] + [vp] * 5 + [i64, i64] + [vp] * 2 + [vp]
         lib.ep_get_group_layout.restype = ctypes.c_int
-        lib.ep_get_group_layout.argtypes = [P, vp, i64, vp, vp]
+        lib.ep_get_group_layout.argtypes = [P, vp, i64, vp, vp, vp]
         lib.ep_dispatch_hier.restype = ctypes.c_int
         lib.ep_dispatch_hier.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp]
         lib.ep_combine_hier.restype = ctypes.c_int
@@ -200,23 +200,26 @@ class BoundCall:
     """One entry point with its arguments marshalled once.  Calling it issues
     the same C call again (same pointers, sizes and stream), so a loop that
     repeats a step pays only for the call itself.  The tensors must stay
-    alive and in place while it is used; the problem struct is passed by
-    reference, so later changes to it are seen."""
+    alive and in place while it is used.  The problem is copied when the
+    call is bound: the tensors were checked against its sizes then, so later
+    changes to the caller's struct are not seen (bind again instead)."""
 
-    def __init__(self, name: str, args: tuple):
+    def __init__(self, name: str, problem: Problem, args: tuple):
         self.name = name
         self._fn = getattr(load(), name)
-        self._args = args
+        self.problem = Problem.from_buffer_copy(problem)
+        self._args = (ctypes.byref(self.problem), *args)
 
     def __call__(self) -> int:
         return _check(self._fn(*self._args), self.name)
 
 
-def _run(name: str, args: tuple, bind: bool):
-    """Calls the entry point now, or with bind=True returns it as a BoundCall."""
+def _run(name: str, problem: Problem, args: tuple, bind: bool):
+    """Calls the entry point on `problem` and args now, or with bind=True
+    returns it as a BoundCall."""
     if bind:
-        return BoundCall(name, args)
-    return _check(getattr(load(), name)(*args), name)
+        return BoundCall(name, problem, args)
+    return _check(getattr(load(), name)(ctypes.byref(problem), *args), name)
 
 
 def ep_workspace_bytes(problem: Problem) -> int:
@@ -233,7 +236,7 @@ def ep_get_layout(problem, topk_idx, expert_count, expert_offset, rank_row_count
     lay = _layout_ptrs(problem, topk_idx, expert_count, expert_offset, rank_row_count,
                        rank_token_count, group_token_count, is_token_in_rank, token_slot,
                        cumulative_expert_recv, workspace, workspace_bytes)
-    return _run("ep_get_layout", (ctypes.byref(problem), *lay, _stream(stream)), bind)
+    return _run("ep_get_layout", problem, (*lay, _stream(stream)), bind)
 
 
 def _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight):
@@ -247,8 +250,8 @@ def ep_dispatch(problem, x, topk_weights, token_slot, recv_x, recv_src_token=Non
                 recv_weight=None, stream=None, bind=False):
     T, _, K, _, _, _, _ = _sizes(problem)
     px, pw, prx, psrc, prw = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
-    return _run("ep_dispatch", (ctypes.byref(problem), px, pw, _arg(token_slot, "token_slot", "int32", T * K),
-                                prx, psrc, prw, _stream(stream)), bind)
+    return _run("ep_dispatch", problem, (px, pw, _arg(token_slot, "token_slot", "int32", T * K),
+        prx, psrc, prw, _stream(stream)), bind)
 
 
 def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_count,
@@ -260,22 +263,22 @@ def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_
                        rank_token_count, group_token_count, is_token_in_rank, token_slot,
                        cumulative_expert_recv, workspace, workspace_bytes)
     rows = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
-    return _run("ep_layout_dispatch", (ctypes.byref(problem), *lay, *rows, _stream(stream)), bind)
+    return _run("ep_layout_dispatch", problem, (*lay, *rows, _stream(stream)), bind)
 
 
 def ep_combine(problem, y, token_slot, topk_weights, out, stream=None, bind=False):
     T, H, K, _, _, _, rows = _sizes(problem)
-    return _run("ep_combine", (ctypes.byref(problem), _arg(y, "y", "bf16", rows * H),
-                               _arg(token_slot, "token_slot", "int32", T * K),
-                               _arg(topk_weights, "topk_weights", "float", T * K),
-                               _arg(out, "out", "bf16", T * H), _stream(stream)), bind)
+    return _run("ep_combine", problem, (_arg(y, "y", "bf16", rows * H),
+        _arg(token_slot, "token_slot", "int32", T * K),
+        _arg(topk_weights, "topk_weights", "float", T * K),
+        _arg(out, "out", "bf16", T * H), _stream(stream)), bind)
 
 
 def ep_quantize_fp8(problem, x, x_fp8, x_sf, stream=None, bind=False):
     T, H, _, _, _, _, _ = _sizes(problem)
-    return _run("ep_quantize_fp8", (ctypes.byref(problem), _arg(x, "x", "bf16", T * H),
-                                    _arg(x_fp8, "x_fp8", "e4m3", T * H),
-                                    _arg(x_sf, "x_sf", "float", T * (H // 128)), _stream(stream)), bind)
+    return _run("ep_quantize_fp8", problem, (_arg(x, "x", "bf16", T * H),
+        _arg(x_fp8, "x_fp8", "e4m3", T * H),
+        _arg(x_sf, "x_sf", "float", T * (H // 128)), _stream(stream)), bind)
 
 
 def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, recv_sf,
@@ -284,12 +287,12 @@ def ep_dispatch_fp8(problem, x_fp8, x_sf, topk_weights, token_slot, recv_x_fp8, 
     T, _, K, _, _, _, rows = _sizes(problem)
     px, psf, prx, prsf = _fp8_rows_ptrs(problem, x_fp8, x_sf, recv_x_fp8, recv_sf, sf_token_stride,
                                         sf_hidden_stride)
-    return _run("ep_dispatch_fp8", (ctypes.byref(problem), px, psf,
-                                    _arg(topk_weights, "topk_weights", "float", T * K),
-                                    _arg(token_slot, "token_slot", "int32", T * K), prx, prsf,
-                                    sf_token_stride, sf_hidden_stride,
-                                    _arg(recv_src_token, "recv_src_token", "int32", rows),
-                                    _arg(recv_weight, "recv_weight", "float", rows), _stream(stream)), bind)
+    return _run("ep_dispatch_fp8", problem, (px, psf,
+        _arg(topk_weights, "topk_weights", "float", T * K),
+        _arg(token_slot, "token_slot", "int32", T * K), prx, prsf,
+        sf_token_stride, sf_hidden_stride,
+        _arg(recv_src_token, "recv_src_token", "int32", rows),
+        _arg(recv_weight, "recv_weight", "float", rows), _stream(stream)), bind)
 
 
 def ep_layout_dispatch_fp8(problem, topk_idx, expert_count, expert_offset, rank_row_count,
@@ -304,53 +307,56 @@ def ep_layout_dispatch_fp8(problem, topk_idx, expert_count, expert_offset, rank_
                        cumulative_expert_recv, workspace, workspace_bytes)
     px, psf, prx, prsf = _fp8_rows_ptrs(problem, x_fp8, x_sf, recv_x_fp8, recv_sf, sf_token_stride,
                                         sf_hidden_stride)
-    return _run("ep_layout_dispatch_fp8", (ctypes.byref(problem), *lay, px, psf,
-                                           _arg(topk_weights, "topk_weights", "float", T * K), prx, prsf,
-                                           sf_token_stride, sf_hidden_stride,
-                                           _arg(recv_src_token, "recv_src_token", "int32", rows),
-                                           _arg(recv_weight, "recv_weight", "float", rows),
-                                           _stream(stream)), bind)
+    return _run("ep_layout_dispatch_fp8", problem, (*lay, px, psf,
+        _arg(topk_weights, "topk_weights", "float", T * K), prx, prsf,
+        sf_token_stride, sf_hidden_stride,
+        _arg(recv_src_token, "recv_src_token", "int32", rows),
+        _arg(recv_weight, "recv_weight", "float", rows),
+        _stream(stream)), bind)
 
 
-def ep_get_group_layout(problem, is_token_in_rank, group_stride_rows, group_slot,
+def ep_get_group_layout(problem, is_token_in_rank, group_stride_rows, group_slot, status=None,
                         stream=None, bind=False):
+    """Group slots of the two-level path; `status` (one int32 on the device,
+    e.g. the layout's workspace) is lowered to EP_ERR_CAPACITY when a group
+    overflows SG rows."""
     T, _, _, _, R, G, _ = _sizes(problem)
-    return _run("ep_get_group_layout", (ctypes.byref(problem),
-                                        _arg(is_token_in_rank, "is_token_in_rank", "uint8", T * R),
-                                        group_stride_rows, _arg(group_slot, "group_slot", "int32", T * G),
-                                        _stream(stream)), bind)
+    return _run("ep_get_group_layout", problem, (
+        _arg(is_token_in_rank, "is_token_in_rank", "uint8", T * R),
+        group_stride_rows, _arg(group_slot, "group_slot", "int32", T * G),
+        _arg(status, "status", "bytes", 4), _stream(stream)), bind)
 
 
 def ep_dispatch_hier(problem, x, topk_weights, token_slot, group_slot, group_stride_rows,
                      group_buf, recv_x, recv_src_token=None, recv_weight=None, stream=None, bind=False):
     T, H, K, _, _, G, _ = _sizes(problem)
     px, pw, prx, psrc, prw = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
-    return _run("ep_dispatch_hier", (ctypes.byref(problem), px, pw,
-                                     _arg(token_slot, "token_slot", "int32", T * K),
-                                     _arg(group_slot, "group_slot", "int32", T * G), group_stride_rows,
-                                     _arg(group_buf, "group_buf", "bf16", G * group_stride_rows * H),
-                                     prx, psrc, prw, _stream(stream)), bind)
+    return _run("ep_dispatch_hier", problem, (px, pw,
+        _arg(token_slot, "token_slot", "int32", T * K),
+        _arg(group_slot, "group_slot", "int32", T * G), group_stride_rows,
+        _arg(group_buf, "group_buf", "bf16", G * group_stride_rows * H),
+        prx, psrc, prw, _stream(stream)), bind)
 
 
 def ep_combine_hier(problem, y, token_slot, topk_weights, group_slot, group_stride_rows,
                     group_buf, out, stream=None, bind=False):
     T, H, K, _, _, G, rows = _sizes(problem)
-    return _run("ep_combine_hier", (ctypes.byref(problem), _arg(y, "y", "bf16", rows * H),
-                                    _arg(token_slot, "token_slot", "int32", T * K),
-                                    _arg(topk_weights, "topk_weights", "float", T * K),
-                                    _arg(group_slot, "group_slot", "int32", T * G), group_stride_rows,
-                                    _arg(group_buf, "group_buf", "bf16", G * group_stride_rows * H),
-                                    _arg(out, "out", "bf16", T * H), _stream(stream)), bind)
+    return _run("ep_combine_hier", problem, (_arg(y, "y", "bf16", rows * H),
+        _arg(token_slot, "token_slot", "int32", T * K),
+        _arg(topk_weights, "topk_weights", "float", T * K),
+        _arg(group_slot, "group_slot", "int32", T * G), group_stride_rows,
+        _arg(group_buf, "group_buf", "bf16", G * group_stride_rows * H),
+        _arg(out, "out", "bf16", T * H), _stream(stream)), bind)
 
 
 def ep_combine_topk_weights(problem, recv_weight, token_slot, combined_topk_weights,
                             stream=None, bind=False):
     T, _, K, _, _, _, rows = _sizes(problem)
-    return _run("ep_combine_topk_weights", (ctypes.byref(problem),
-                                            _arg(recv_weight, "recv_weight", "float", rows),
-                                            _arg(token_slot, "token_slot", "int32", T * K),
-                                            _arg(combined_topk_weights, "combined_topk_weights", "float",
-                                                 T * K), _stream(stream)), bind)
+    return _run("ep_combine_topk_weights", problem, (
+        _arg(recv_weight, "recv_weight", "float", rows),
+        _arg(token_slot, "token_slot", "int32", T * K),
+        _arg(combined_topk_weights, "combined_topk_weights", "float",
+        T * K), _stream(stream)), bind)
 
 
 def ep_read_status(workspace, stream=None) -> int:

@@ -36,6 +36,12 @@ int check_shape(const ep_problem *p) {
     // index arithmetic in the kernels overshoots the last entry or token by
     // less than a tile (at most 16384) before it is clamped or tested
     if (entries + pad > INT32_MAX - (1 << 16)) return EP_ERR_INVALID_ARG;
+    // the chunk table is read through raw buffer loads with 32-bit byte
+    // offsets, and an offset past the table (0xFFFFFFFC) must stay out of
+    // range for predicated loads: fewer than 2^30 table entries
+    const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts, p->num_ranks,
+                                        p->num_groups);
+    if (w.nchunks * w.pitch >= (int64_t{1} << 30)) return EP_ERR_INVALID_ARG;
     return EP_OK;
 }
 
@@ -92,8 +98,6 @@ int layout_params(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_
     lp.L = p->num_experts / p->num_ranks;
     lp.ranks_per_group = p->num_ranks / p->num_groups;
     lp.div_L = epget::FastDiv::make(static_cast<uint32_t>(lp.L));
-    lp.div_R = epget::FastDiv::make(static_cast<uint32_t>(lp.R));
-    lp.div_G = epget::FastDiv::make(static_cast<uint32_t>(lp.G));
     lp.S = static_cast<int32_t>(p->rank_stride_rows);
     lp.chunk_tokens = w.chunk_tokens;
     lp.nchunks = static_cast<int32_t>(w.nchunks);
@@ -338,15 +342,17 @@ epget::HierParams hier_params(const ep_problem *p, int64_t SG) {
 extern "C" {
 
 int ep_get_group_layout(const ep_problem *p, const uint8_t *is_token_in_rank,
-                        int64_t group_stride_rows, int32_t *group_slot, void *stream) {
+                        int64_t group_stride_rows, int32_t *group_slot, int32_t *status,
+                        void *stream) {
     int rc = check_problem(p);
     if (rc != EP_OK) return rc;
     if ((rc = check_groups(p, group_stride_rows)) != EP_OK) return rc;
+    if (!aligned(status, 4)) return EP_ERR_INVALID_ARG;
     if (p->num_tokens == 0) return EP_OK;
     if (!is_token_in_rank || !group_slot || !aligned(group_slot, 4)) return EP_ERR_INVALID_ARG;
     return hip_rc(epget::launch_group_layout(p->num_tokens, p->num_ranks,
                                              hier_params(p, group_stride_rows), is_token_in_rank,
-                                             group_slot, static_cast<hipStream_t>(stream)));
+                                             group_slot, status, static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch_hier(const ep_problem *p, const uint16_t *x, const float *topk_weights,

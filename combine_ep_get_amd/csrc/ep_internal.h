@@ -53,7 +53,7 @@ struct FastDiv {
 struct LayoutParams {
     const int32_t *topk_idx;
     int32_t T, K, E, R, G, A, L, ranks_per_group;
-    FastDiv div_L, div_R, div_G;
+    FastDiv div_L;
     int32_t S;
     int32_t chunk_tokens, nchunks, ncols, pitch, nbits;
     int32_t *expert_count, *expert_offset, *rank_row_count, *rank_token_count;

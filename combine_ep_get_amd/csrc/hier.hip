@@ -34,7 +34,8 @@ constexpr int kGroupTpt = 16;  // flags per thread in the scan
 template <bool kWords, int NT>
 __global__ __launch_bounds__(NT) void group_layout_kernel(int32_t T, int32_t R, HierParams h,
                                                           const uint8_t *__restrict__ map,
-                                                          int32_t *__restrict__ group_slot) {
+                                                          int32_t *__restrict__ group_slot,
+                                                          int32_t *__restrict__ status) {
     constexpr int kPass = NT * kGroupTpt;
     __shared__ __align__(16) uint8_t s_flag[kPass];
     __shared__ int s_first[NT];
@@ -100,6 +101,9 @@ __global__ __launch_bounds__(NT) void group_layout_kernel(int32_t T, int32_t R, 
         carry += total;
         __syncthreads();  // LDS is rewritten by the next pass
     }
+    // more tokens reach the group than it has rows: lower the status to the
+    // capacity error, keeping a lower (bad-id) code already there
+    if (status && i == 0 && carry > h.SG) atomicMin(status, EP_ERR_CAPACITY);
 }
 
 // Group slots of a batch of more than 4096 tokens: tiles of kTileTokens
@@ -118,7 +122,8 @@ constexpr int kTileTokens = kTileThreads * kTileTpt;
 template <bool kWords>
 __global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, int32_t R, HierParams h,
                                                                    const uint8_t *__restrict__ map,
-                                                                   int32_t *__restrict__ group_slot) {
+                                                                   int32_t *__restrict__ group_slot,
+                                                                   int32_t *__restrict__ status) {
     __shared__ uint8_t s_flag[kTileTokens];
     __shared__ int s_first[kTileThreads];
     __shared__ uint32_t s_bits[kTileThreads];
@@ -182,6 +187,9 @@ __global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, in
     for (int q = 0; q < kTileThreads / 64; ++q) before += q < w ? s_wsum[q] : 0;
     s_first[i] = carry + before + incl - n;
     s_bits[i] = bits;
+    // the last thread's count runs to the end of the tile: past SG, the
+    // group overflows (as in group_layout_kernel)
+    if (status && i == kTileThreads - 1 && carry + before + incl > h.SG) atomicMin(status, EP_ERR_CAPACITY);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kTileTpt; ++k) {
@@ -199,14 +207,14 @@ __global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, in
 
 template <bool kWords>
 void launch_group_layout_nt(int32_t T, int32_t R, const HierParams &h, const uint8_t *map, int32_t *group_slot,
-                            hipStream_t stream) {
+                            int32_t *status, hipStream_t stream) {
     if (T <= 64 * kGroupTpt) {
-        group_layout_kernel<kWords, 64><<<h.G, 64, 0, stream>>>(T, R, h, map, group_slot);
+        group_layout_kernel<kWords, 64><<<h.G, 64, 0, stream>>>(T, R, h, map, group_slot, status);
     } else if (T <= 256 * kGroupTpt) {
-        group_layout_kernel<kWords, 256><<<h.G, 256, 0, stream>>>(T, R, h, map, group_slot);
+        group_layout_kernel<kWords, 256><<<h.G, 256, 0, stream>>>(T, R, h, map, group_slot, status);
     } else {
         const dim3 grid((T + kTileTokens - 1) / kTileTokens, h.G);
-        group_tiles_kernel<kWords><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot);
+        group_tiles_kernel<kWords><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot, status);
     }
 }
 
@@ -402,7 +410,9 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_groups_kernel(
 }
 
 // Two-level dispatch, stage 2: each group row of the token goes to the
-// entries of that group (with the entry's source index and weight).  With
+// entries of that group (with the entry's source index and weight; an entry
+// whose group row was dropped for capacity gets source -1 and weight 0, and
+// its row is not written).  With
 // few groups each (token, group) has workgroups of its own (blockIdx.z = g),
 // so a token's groups are expanded side by side rather than one after the
 // other: on a 16384-token step with two groups the dispatch took 10 µs less
@@ -420,8 +430,12 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, Hier
     if (blockIdx.y == 0 && blockIdx.z == 0 && static_cast<int>(threadIdx.x) < c.K) {
         const int j = threadIdx.x;  // lane j of wave 0
         if (slot_ok(lane_slot, c.num_rows)) {
-            if (a.recv_src) a.recv_src[lane_slot] = t;
-            if (a.recv_w) a.recv_w[lane_slot] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+            const int g = (lane_slot / h.S) / h.ranks_per_group;
+            const int32_t gs = group_slot[static_cast<int64_t>(t) * h.G + g];
+            const bool kept = gs >= 0 && gs < h.group_rows;
+            if (a.recv_src) a.recv_src[lane_slot] = kept ? t : -1;
+            if (a.recv_w)
+                a.recv_w[lane_slot] = !kept ? 0.0f : a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
         }
     }
     auto body = [&](int g, int32_t gs) {
@@ -453,11 +467,11 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(CopyParams c, Hier
 }  // namespace
 
 hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
-                               int32_t *group_slot, hipStream_t stream) {
+                               int32_t *group_slot, int32_t *status, hipStream_t stream) {
     if (h.ranks_per_group % 4 == 0 && reinterpret_cast<uintptr_t>(map) % 4 == 0)
-        launch_group_layout_nt<true>(T, R, h, map, group_slot, stream);
+        launch_group_layout_nt<true>(T, R, h, map, group_slot, status, stream);
     else
-        launch_group_layout_nt<false>(T, R, h, map, group_slot, stream);
+        launch_group_layout_nt<false>(T, R, h, map, group_slot, status, stream);
     return hipGetLastError();
 }
 

@@ -13,8 +13,10 @@ struct HierParams {
     int64_t group_rows;
 };
 
+// status (may be null): lowered to EP_ERR_CAPACITY when a group has more
+// tokens than SG rows.
 hipError_t launch_group_layout(int32_t T, int32_t R, const HierParams &h, const uint8_t *map,
-                               int32_t *group_slot, hipStream_t stream);
+                               int32_t *group_slot, int32_t *status, hipStream_t stream);
 // Stage-1 dispatch: each token's row to its group rows.
 hipError_t launch_group_dispatch(const CopyParams &c, const HierParams &h, const uint16_t *x,
                                  const int32_t *group_slot, uint16_t *group_buf, hipStream_t stream);

@@ -59,6 +59,7 @@ extern "C" {
 #define EP_ERR_CAPACITY (-3)    /* some rank needs more than S rows (device-detected) */
 #define EP_ERR_BAD_EXPERT (-4)  /* an id outside [0,E) other than -1 (device-detected) */
 
+
 /* Limits of [V2] (kNumMaxRanks, kNumMaxExperts, kNumMaxExpertsPerRank)
  * and this library's own top-k and hidden-size limits (a row of H bf16
  * must fit the launch grid: 2^24 channels is a 32 MiB row). */
@@ -74,7 +75,11 @@ extern "C" {
  *   1 <= G and R % G == 0; 1 <= K <= 32; A >= 1;
  *   S >= 1; R * S <= INT32_MAX (slots are int32);
  *   T * K + E * A <= INT32_MAX - 65536 (entry and token indices stay int32
- *   with room for the kernels' tiles to run past the end before clamping). */
+ *   with room for the kernels' tiles to run past the end before clamping);
+ *   ceil(T / floor(1024 / K)) * round_up(E + R + G + 1, 64) < 2^30 (the
+ *   layout's table of per-chunk counts is addressed with 32-bit byte
+ *   offsets; this binds only past about 2.6e8 entries at E = 2048,
+ *   R = G = 1024, and never at E <= 256 with R <= 64). */
 typedef struct ep_problem {
     int32_t num_tokens;       /* T: tokens of this source rank */
     int32_t hidden;           /* H: bf16 elements per row, a multiple of 8, <= EP_MAX_HIDDEN */
@@ -267,18 +272,28 @@ int ep_layout_dispatch_fp8(const ep_problem *problem, const int32_t *topk_idx,
  * Requires SG >= 1 and G*SG <= INT32_MAX.
  *
  * ep_get_group_layout: group_slot [T,G] int32 from is_token_in_rank [T,R]
- *   (an output of ep_get_layout).  SG = T never drops a token.
+ *   (an output of ep_get_layout).  SG = T never drops a token.  status: NULL,
+ *   or one int32 on the device, 4-byte aligned (typically the layout's
+ *   workspace, whose first word is the status ep_read_status returns): when
+ *   some group is reached by more than SG tokens, it is lowered to
+ *   EP_ERR_CAPACITY unless it already holds a lower code (EP_ERR_BAD_EXPERT
+ *   stays); it is never raised or cleared, so a standalone word must be set
+ *   to EP_OK first.
  * ep_dispatch_hier: x -> group_buf (one row per token and group), then each
  *   entry's row is copied from its group's row into recv_x; recv_src_token
  *   and recv_weight as in ep_dispatch.  recv_x ends up identical to
- *   ep_dispatch's.
+ *   ep_dispatch's when no group row was dropped.  An entry whose group row
+ *   was dropped (group_slot -1 for its group although the token has an entry
+ *   there) gets recv_src_token -1 and recv_weight 0, and its row of recv_x is
+ *   not written; ep_combine_hier leaves such entries out.
  * ep_combine_hier: per (token, group) the partial sum over the token's
  *   entries in that group, folded in fp32 with FMA in ascending j and rounded
  *   to bf16 into the group row (the value that would cross the scale-out
  *   link); then out[t] = bf16(sum of its group rows), fp32 accumulate.
  *   group_buf is overwritten. */
 int ep_get_group_layout(const ep_problem *problem, const uint8_t *is_token_in_rank,
-                        int64_t group_stride_rows, int32_t *group_slot, void *stream);
+                        int64_t group_stride_rows, int32_t *group_slot, int32_t *status,
+                        void *stream);
 int ep_dispatch_hier(const ep_problem *problem, const uint16_t *x, const float *topk_weights,
                      const int32_t *token_slot, const int32_t *group_slot,
                      int64_t group_stride_rows, uint16_t *group_buf, uint16_t *recv_x,

@@ -64,10 +64,10 @@ def open_library(path: str):
     lib.oracle_quantize_fp8.argtypes = [i32, i32, vp, vp, vp]
     lib.oracle_dispatch_fp8.restype = None
     lib.oracle_dispatch_fp8.argtypes = [i32, i32, i32, i64] + [vp] * 6 + [i64, i64, vp, vp]
-    lib.oracle_group_layout.restype = None
+    lib.oracle_group_layout.restype = ctypes.c_int
     lib.oracle_group_layout.argtypes = [i32, i32, i32, i64, vp, vp]
     lib.oracle_dispatch_hier.restype = None
-    lib.oracle_dispatch_hier.argtypes = [i32, i32, i32, i32, i32, i64, i64] + [vp] * 5
+    lib.oracle_dispatch_hier.argtypes = [i32, i32, i32, i32, i32, i64, i64] + [vp] * 8
     lib.oracle_combine_hier.restype = None
     lib.oracle_combine_hier.argtypes = [i32, i32, i32, i32, i32, i64, i64] + [vp] * 6
     lib.oracle_combine_topk_weights.restype = None
@@ -204,20 +204,26 @@ def combine(y: np.ndarray, token_slot: np.ndarray, topk_weights: np.ndarray | No
     return out
 
 
-def group_layout(is_token_in_rank: np.ndarray, G: int, SG: int) -> np.ndarray:
+def group_layout(is_token_in_rank: np.ndarray, G: int, SG: int, with_status: bool = False):
     """Group slots of the hierarchical path: a stable compaction, per group,
     of the tokens with an entry in the group ([V2] hybrid dispatch; [V1]
-    §3.2 groups of ranks).  ``[T,G]`` int32, -1 where absent or past SG."""
+    §3.2 groups of ranks).  ``[T,G]`` int32, -1 where absent or past SG.
+    With ``with_status`` returns (slots, status): CAPACITY if some group
+    has more than SG tokens, else OK."""
     m = _c(is_token_in_rank, np.uint8)
     T, R = m.shape
     out = np.empty((T, G), np.int32)
-    _load().oracle_group_layout(T, R, G, SG, _p(m), _p(out))
-    return out
+    status = _load().oracle_group_layout(T, R, G, SG, _p(m), _p(out))
+    return (out, status) if with_status else out
 
 
-def dispatch_hier(x, group_slot, token_slot, R, S, SG, recv_x=None):
+def dispatch_hier(x, group_slot, token_slot, R, S, SG, recv_x=None, topk_weights=None,
+                  with_meta=False):
     """Two-level dispatch: rows to the group buffer once per group, then
-    from the group rows to every expert row.  Returns (group_buf, recv_x)."""
+    from the group rows to every expert row.  Returns (group_buf, recv_x),
+    and with ``with_meta`` also (recv_src_token, recv_weight) [R*S], where a
+    row whose group row was dropped gets -1 and 0 (rows no slot names stay
+    -1 and 0 as well)."""
     x = _c(x, np.uint16)
     gsl = _c(group_slot, np.int32)
     slot = _c(token_slot, np.int32)
@@ -227,9 +233,12 @@ def dispatch_hier(x, group_slot, token_slot, R, S, SG, recv_x=None):
     gbuf = np.zeros((G * SG, H), np.uint16)
     if recv_x is None:
         recv_x = np.zeros((R * S, H), np.uint16)
-    _load().oracle_dispatch_hier(T, H, K, R, G, S, SG, _p(x), _p(gsl), _p(slot), _p(gbuf),
-                                 _p(recv_x))
-    return gbuf, recv_x
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    src = np.full(R * S, -1, np.int32)
+    rw = np.zeros(R * S, np.float32)
+    _load().oracle_dispatch_hier(T, H, K, R, G, S, SG, _p(x), _p(w), _p(gsl), _p(slot), _p(gbuf),
+                                 _p(recv_x), _p(src), _p(rw))
+    return (gbuf, recv_x, src, rw) if with_meta else (gbuf, recv_x)
 
 
 def combine_hier(y, token_slot, topk_weights, group_slot, R, S, SG):

@@ -182,10 +182,12 @@ void oracle_dispatch(int32_t T, int32_t H, int32_t K, int64_t num_rows,
  *
  *   group layout: group_slot[t,g] = g*SG + (number of earlier tokens with an
  *     entry in group g) for a token with an entry in group g, else -1 (also
- *     -1 past the group capacity SG);
+ *     -1 past the group capacity SG, and the status is then ORACLE_CAPACITY);
  *   dispatch: x[t] -> group_buf[group_slot[t,g]], then each entry's row is
  *     copied from its group's row: recv_x[token_slot[t,j]] =
- *     group_buf[group_slot[t, group of token_slot[t,j]]];
+ *     group_buf[group_slot[t, group of token_slot[t,j]]]; the received row
+ *     carries source token t and weight w[t,j], or -1 and 0 when its group
+ *     row was dropped for capacity (the row itself is then not written);
  *   combine: per (t,g) a partial sum over the entries in group g, folded in
  *     fp32 with fused multiply-add in ascending j and rounded to bf16 in
  *     group_buf (the value that would cross the scale-out link), then
@@ -195,10 +197,11 @@ void oracle_dispatch(int32_t T, int32_t H, int32_t K, int64_t num_rows,
  * it is computed in the kernel's precision (fp32 FMA); the final sum over
  * groups is in double.
  */
-void oracle_group_layout(int32_t T, int32_t R, int32_t G, int64_t SG,
-                         const uint8_t *is_token_in_rank, int32_t *group_slot)
+int oracle_group_layout(int32_t T, int32_t R, int32_t G, int64_t SG,
+                        const uint8_t *is_token_in_rank, int32_t *group_slot)
 {
     const int32_t rpg = R / G;
+    int over = 0;
     for (int32_t g = 0; g < G; ++g) {
         int64_t pos = 0;
         for (int64_t t = 0; t < T; ++t) {
@@ -209,15 +212,19 @@ void oracle_group_layout(int32_t T, int32_t R, int32_t G, int64_t SG,
             group_slot[t * G + g] = pos < SG ? (int32_t)(g * SG + pos) : -1;
             pos += 1;
         }
+        if (pos > SG) over = 1;
     }
+    return over ? ORACLE_CAPACITY : ORACLE_OK;
 }
 
 /* group of a valid slot: rank = slot / S, group = rank / (R/G) */
 static int32_t slot_group(int64_t s, int64_t S, int32_t R, int32_t G) { return (int32_t)((s / S) / (R / G)); }
 
 void oracle_dispatch_hier(int32_t T, int32_t H, int32_t K, int32_t R, int32_t G, int64_t S,
-                          int64_t SG, const uint16_t *x, const int32_t *group_slot,
-                          const int32_t *token_slot, uint16_t *group_buf, uint16_t *recv_x)
+                          int64_t SG, const uint16_t *x, const float *topk_weights,
+                          const int32_t *group_slot, const int32_t *token_slot,
+                          uint16_t *group_buf, uint16_t *recv_x, int32_t *recv_src_token,
+                          float *recv_weight)
 {
     const int64_t num_rows = (int64_t)R * S, group_rows = (int64_t)G * SG;
     for (int64_t t = 0; t < T; ++t)
@@ -230,8 +237,11 @@ void oracle_dispatch_hier(int32_t T, int32_t H, int32_t K, int32_t R, int32_t G,
             int64_t s = token_slot[t * K + j];
             if (s < 0 || s >= num_rows) continue;
             int64_t gs = group_slot[t * G + slot_group(s, S, R, G)];
-            if (gs < 0 || gs >= group_rows) continue;
-            memcpy(recv_x + s * H, group_buf + gs * H, (size_t)H * 2);
+            int kept = gs >= 0 && gs < group_rows;
+            if (recv_src_token) recv_src_token[s] = kept ? (int32_t)t : -1;
+            if (recv_weight)
+                recv_weight[s] = !kept ? 0.0f : topk_weights ? topk_weights[t * K + j] : 1.0f;
+            if (kept) memcpy(recv_x + s * H, group_buf + gs * H, (size_t)H * 2);
         }
 }
 

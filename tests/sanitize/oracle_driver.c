@@ -29,11 +29,13 @@ void oracle_dispatch_fp8(int32_t T, int32_t H, int32_t K, int64_t num_rows, cons
                          const float *sf, const float *topk_weights, const int32_t *token_slot,
                          uint8_t *recv_q, float *recv_sf, int64_t sf_token_stride,
                          int64_t sf_hidden_stride, int32_t *recv_src_token, float *recv_weight);
-void oracle_group_layout(int32_t T, int32_t R, int32_t G, int64_t SG,
-                         const uint8_t *is_token_in_rank, int32_t *group_slot);
+int oracle_group_layout(int32_t T, int32_t R, int32_t G, int64_t SG,
+                        const uint8_t *is_token_in_rank, int32_t *group_slot);
 void oracle_dispatch_hier(int32_t T, int32_t H, int32_t K, int32_t R, int32_t G, int64_t S,
-                          int64_t SG, const uint16_t *x, const int32_t *group_slot,
-                          const int32_t *token_slot, uint16_t *group_buf, uint16_t *recv_x);
+                          int64_t SG, const uint16_t *x, const float *topk_weights,
+                          const int32_t *group_slot, const int32_t *token_slot,
+                          uint16_t *group_buf, uint16_t *recv_x, int32_t *recv_src_token,
+                          float *recv_weight);
 void oracle_combine_hier(int32_t T, int32_t H, int32_t K, int32_t R, int32_t G, int64_t S,
                          int64_t SG, const uint16_t *y, const int32_t *token_slot,
                          const float *topk_weights, const int32_t *group_slot,
@@ -126,9 +128,10 @@ int main(void) {
         oracle_dispatch_fp8(T, H, K, rows, q, sf, NULL, slot, rq, rsf, 1, rows, NULL, NULL);
 
         int32_t *gslot = alloc((size_t)T * G, 4);
-        oracle_group_layout(T, R, G, SG, map, gslot);
+        (void)oracle_group_layout(T, R, G, SG, map, gslot);
         uint16_t *gbuf = alloc((size_t)G * SG * H, 2);
-        oracle_dispatch_hier(T, H, K, R, G, S, SG, x, gslot, slot, gbuf, recv);
+        oracle_dispatch_hier(T, H, K, R, G, S, SG, x, w, gslot, slot, gbuf, recv, src, rw);
+        oracle_dispatch_hier(T, H, K, R, G, S, SG, x, NULL, gslot, slot, gbuf, recv, NULL, NULL);
         oracle_combine_hier(T, H, K, R, G, S, SG, recv, slot, w, gslot, gbuf, out);
 
         free(idx); free(x); free(w); free(cnt); free(off); free(rrc); free(rtc); free(gtc);

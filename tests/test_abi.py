@@ -57,6 +57,8 @@ def test_stride_hint_and_workspace():
     dict(K=0), dict(K=33), dict(H=7), dict(H=0), dict(H=(1 << 24) + 8), dict(T=-1), dict(G=3), dict(G=0),
     dict(A=0), dict(S=0), dict(S=2**31 // 8 + 1),
     dict(T=(2**31 - 1 - 2**16 - 256) // 8 + 1, S=1),      # T*K + E*A one tile short of int32
+    # one chunk of 128 tokens past a 2^30-entry count table (pitch 4160)
+    dict(T=258111 * 128 + 1, E=2048, R=1024, G=1024, S=1),
 ])
 def test_invalid_problems_rejected_before_launch(bad):
     p = P(**bad)
@@ -68,6 +70,18 @@ def test_invalid_problems_rejected_before_launch(bad):
     assert lib.ep_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(p), fake, fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine_topk_weights(ctypes.byref(p), fake, fake, fake, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_count_table_limit():
+    """The largest chunk table the layout addresses with 32-bit offsets:
+    258111 chunks of 128 tokens x 4160 columns is under 2^30 entries, one
+    more chunk is not."""
+    big = dict(E=2048, R=1024, G=1024, S=1)
+    assert ep.ep_workspace_bytes(P(T=258111 * 128, **big)) > 0
+    assert ep.ep_workspace_bytes(P(T=258111 * 128 + 1, **big)) == 0
+    # one token per layout chunk at K = 32; the table grows with T
+    assert ep.ep_workspace_bytes(P(T=258111 * 32, K=32, **big)) > 0
+    assert ep.ep_workspace_bytes(P(T=258111 * 32 + 1, K=32, **big)) == 0
 
 
 def test_reserved_field_must_be_zero():

@@ -50,10 +50,16 @@ def test_group_slots(name, G):
     gs = oracle.group_layout(lay.is_token_in_rank, G, T)
     np.testing.assert_array_equal(gs, restated_group_slots(lay.is_token_in_rank, G, T))
     np.testing.assert_array_equal((gs >= 0).sum(0), lay.group_token_count)
-    # capacity: a smaller group slice drops the later tokens
+    assert oracle.group_layout(lay.is_token_in_rank, G, T, with_status=True)[1] == oracle.OK
+    # capacity: a smaller group slice drops the later tokens and reports it;
+    # exactly the fullest group's count does not
     SG = int(lay.group_token_count.min()) - 1
-    gs2 = oracle.group_layout(lay.is_token_in_rank, G, SG)
+    gs2, st = oracle.group_layout(lay.is_token_in_rank, G, SG, with_status=True)
     np.testing.assert_array_equal(gs2, restated_group_slots(lay.is_token_in_rank, G, SG))
+    assert st == oracle.CAPACITY
+    full = int(lay.group_token_count.max())
+    assert oracle.group_layout(lay.is_token_in_rank, G, full, with_status=True)[1] == oracle.OK
+    assert oracle.group_layout(lay.is_token_in_rank, G, full - 1, with_status=True)[1] == oracle.CAPACITY
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill4k"])
@@ -68,6 +74,31 @@ def test_two_level_dispatch_equals_flat(name):
     # every group row holds its token's row
     t_idx, g_idx = np.nonzero(gs >= 0)
     assert np.array_equal(gbuf[gs[t_idx, g_idx]], inp.x[t_idx])
+
+
+def test_two_level_dispatch_marks_dropped_entries():
+    """With a group capacity below the fullest group, every entry keeps its
+    flat row and metadata exactly when its token kept a row in the entry's
+    group; the others get source -1, weight 0 and no row."""
+    inp, wl, S, lay = _setup("prefill4k")
+    G = 4
+    lay = oracle.layout(inp.topk_idx, wl.E, wl.R, S, G)
+    SG = int(lay.group_token_count.min()) - 50
+    gs = oracle.group_layout(lay.is_token_in_rank, G, SG)
+    _, rx, src, rw = oracle.dispatch_hier(inp.x, gs, lay.token_slot, wl.R, S, SG,
+                                          topk_weights=inp.topk_weights, with_meta=True)
+    flat, fsrc, frw = oracle.dispatch(inp.x, lay.token_slot, wl.R * S, inp.topk_weights)
+    T, K = lay.token_slot.shape
+    t_of = np.repeat(np.arange(T), K).reshape(T, K)
+    slot = lay.token_slot
+    grp = (slot // S) // (wl.R // G)
+    kept = gs[t_of, grp] >= 0
+    assert 0 < (~kept).sum() < kept.sum()
+    s_kept, s_drop = slot[kept], slot[~kept]
+    assert np.array_equal(rx[s_kept], flat[s_kept])
+    assert np.array_equal(src[s_kept], fsrc[s_kept]) and np.array_equal(rw[s_kept], frw[s_kept])
+    assert np.all(src[s_drop] == -1) and np.all(rw[s_drop] == 0)
+    assert not np.any(rx[s_drop])
 
 
 def test_two_level_combine_one_hot_returns_x():

@@ -47,25 +47,34 @@ def run(ep, idx, w, x, E, R, G, S, SG, y=None):
     ep.ep_get_layout(p, dev(idx), *bufs.args())
     ref = oracle.layout(idx, E, R, S, G)
     gslot = torch.empty((T, G), dtype=torch.int32, device="cuda")
-    ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot)
-    torch.cuda.synchronize()
-    ref_gs = oracle.group_layout(ref.is_token_in_rank, G, SG)
+    # the group overflow status goes to the layout's status word
+    ep.ep_get_group_layout(p, bufs.is_token_in_rank, SG, gslot, bufs.workspace)
+    status = ep.ep_read_status(bufs.workspace)
+    ref_gs, ref_gstatus = oracle.group_layout(ref.is_token_in_rank, G, SG, with_status=True)
     assert_same(bufs.token_slot.cpu().numpy(), ref.token_slot)
     assert_same(gslot.cpu().numpy(), ref_gs)
+    assert status == min(ref.status, ref_gstatus), (status, ref.status, ref_gstatus)
     # dispatch
     gbuf = torch.zeros((G * SG, H), dtype=torch.int16, device="cuda")
     recv = torch.zeros((R * S, H), dtype=torch.int16, device="cuda")
     src = torch.full((R * S,), -1, dtype=torch.int32, device="cuda")
+    rw = torch.zeros(R * S, dtype=torch.float32, device="cuda")
     d_w = dev(w)
-    ep.ep_dispatch_hier(p, dev(x.view(np.int16)), d_w, bufs.token_slot, gslot, SG, gbuf, recv, src, None)
+    ep.ep_dispatch_hier(p, dev(x.view(np.int16)), d_w, bufs.token_slot, gslot, SG, gbuf, recv, src, rw)
     torch.cuda.synchronize()
-    ref_gbuf, ref_rx = oracle.dispatch_hier(x, ref_gs, ref.token_slot, R, S, SG)
+    ref_gbuf, ref_rx, ref_src, ref_rw = oracle.dispatch_hier(x, ref_gs, ref.token_slot, R, S, SG,
+                                                             topk_weights=w, with_meta=True)
     valid_g = ref_gs[ref_gs >= 0]
     assert_same(u16(gbuf)[valid_g], ref_gbuf[valid_g])
     s = ref.token_slot[ref.token_slot >= 0]
-    assert_same(u16(recv)[s], ref_rx[s])
-    t_of = np.repeat(np.arange(T), K).reshape(T, K)[ref.token_slot >= 0]
-    assert_same(src.cpu().numpy()[s], t_of)
+    # rows of entries whose group row was dropped are not written
+    kept = s[ref_src[s] >= 0]
+    assert_same(u16(recv)[kept], ref_rx[kept])
+    assert_same(src.cpu().numpy()[s], ref_src[s])
+    assert_same(rw.cpu().numpy()[s].view(np.int32), ref_rw[s].view(np.int32))
+    if ref_gstatus == oracle.OK:
+        t_of = np.repeat(np.arange(T), K).reshape(T, K)[ref.token_slot >= 0]
+        assert_same(ref_src[s], t_of)
     # combine
     if y is None:
         y = ep_inputs.permuted_rows(ref_rx, seed=13)
@@ -102,6 +111,10 @@ def test_hier_small_group_capacity_and_empty_entries(ep):
     S = int(counts.reshape(R, -1).sum(1).max())
     ref = oracle.layout(idx, E, R, S, G)
     SG = int(ref.group_token_count.min()) - 10   # the later tokens of each group are dropped
+    run(ep, idx, w, x, E, R, G, S, SG)
+    # a bad id on top: the layout's bad-id status is kept, not replaced by the
+    # group overflow
+    idx[5, 2] = E + 1
     run(ep, idx, w, x, E, R, G, S, SG)
 
 
@@ -168,6 +181,9 @@ def test_group_layout_maps(ep, T, R, G, density, offset):
         flat = torch.zeros(T * R + offset, dtype=torch.uint8, device="cuda")
         flat[offset:] = dev(m.ravel())
         gslot = torch.empty((T, G), dtype=torch.int32, device="cuda")
-        ep.ep_get_group_layout(p, flat[offset:].view(T, R), SG, gslot)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ep.ep_get_group_layout(p, flat[offset:].view(T, R), SG, gslot, status)
         torch.cuda.synchronize()
-        assert_same(gslot.cpu().numpy(), oracle.group_layout(m, G, SG), f"SG={SG}")
+        want, want_status = oracle.group_layout(m, G, SG, with_status=True)
+        assert_same(gslot.cpu().numpy(), want, f"SG={SG}")
+        assert int(status.item()) == want_status, f"SG={SG}"
