@@ -18,6 +18,8 @@ EP_ERR_INVALID_ARG = -1
 EP_ERR_HIP = -2
 EP_ERR_CAPACITY = -3
 EP_ERR_BAD_EXPERT = -4
+EP_ERR_SCRATCH_LIMIT = -5
+EP_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 EP_MAX_RANKS = 1024
 EP_MAX_EXPERTS = 2048
@@ -29,7 +31,8 @@ EP_MAX_HIDDEN = 1 << 24
 EXPORTS = ("ep_workspace_bytes", "ep_rank_stride_hint", "ep_get_layout", "ep_dispatch",
            "ep_layout_dispatch", "ep_combine", "ep_quantize_fp8", "ep_dispatch_fp8",
            "ep_layout_dispatch_fp8", "ep_get_group_layout", "ep_dispatch_hier", "ep_combine_hier",
-           "ep_combine_topk_weights", "ep_read_status", "ep_error_string")
+           "ep_combine_topk_weights", "ep_read_status", "ep_error_string",
+           "ep_layout_dispatch_noalloc")
 
 
 class EpError(RuntimeError):
@@ -84,6 +87,8 @@ def load():
         lib.ep_dispatch.argtypes = [P] + [vp] * 6 + [vp]
         lib.ep_layout_dispatch.restype = ctypes.c_int
         lib.ep_layout_dispatch.argtypes = [P] + [vp] * 10 + [sz] + [vp] * 5 + [vp]
+        lib.ep_layout_dispatch_noalloc.restype = ctypes.c_int
+        lib.ep_layout_dispatch_noalloc.argtypes = [P] + [vp] * 10 + [vp] * 5 + [vp]
         lib.ep_combine.restype = ctypes.c_int
         lib.ep_combine.argtypes = [P] + [vp] * 4 + [vp]
         lib.ep_quantize_fp8.restype = ctypes.c_int
@@ -264,6 +269,27 @@ def ep_layout_dispatch(problem, topk_idx, expert_count, expert_offset, rank_row_
                        cumulative_expert_recv, workspace, workspace_bytes)
     rows = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
     return _run("ep_layout_dispatch", problem, (*lay, *rows, _stream(stream)), bind)
+
+
+def ep_layout_dispatch_noalloc(problem, topk_idx, expert_count, expert_offset, rank_row_count,
+                               rank_token_count, group_token_count, is_token_in_rank, token_slot,
+                               cumulative_expert_recv, status, x, topk_weights, recv_x,
+                               recv_src_token=None, recv_weight=None, stream=None, bind=False):
+    """ep_layout_dispatch with the layout scratch in the library's static
+    device buffer (no workspace argument); the status word goes to `status`
+    (one int32 on the device, read with ep_read_status)."""
+    T, _, K, E, R, G, _ = _sizes(problem)
+    lay = (_arg(topk_idx, "topk_idx", "int32", T * K), _arg(expert_count, "expert_count", "int32", E),
+           _arg(expert_offset, "expert_offset", "int32", E),
+           _arg(rank_row_count, "rank_row_count", "int32", R),
+           _arg(rank_token_count, "rank_token_count", "int32", R),
+           _arg(group_token_count, "group_token_count", "int32", G),
+           _arg(is_token_in_rank, "is_token_in_rank", "uint8", T * R),
+           _arg(token_slot, "token_slot", "int32", T * K),
+           _arg(cumulative_expert_recv, "cumulative_expert_recv", "int64", E),
+           _arg(status, "status", "int32", 1))
+    rows = _dispatch_ptrs(problem, x, topk_weights, recv_x, recv_src_token, recv_weight)
+    return _run("ep_layout_dispatch_noalloc", problem, (*lay, *rows, _stream(stream)), bind)
 
 
 def ep_combine(problem, y, token_slot, topk_weights, out, stream=None, bind=False):

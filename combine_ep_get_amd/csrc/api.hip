@@ -8,6 +8,9 @@
 // runtime uses ("DeepEP Symmetric Memory 全面架构分析" §7.3, §9.1).
 #include <limits.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/ep_get.h"
 #include "ep_internal.h"
 #include "hier_internal.h"
@@ -244,6 +247,83 @@ int ep_layout_dispatch(const ep_problem *p, const int32_t *topk_idx, int32_t *ex
     return hip_rc(epget::launch_layout_dispatch(lp, copy_params(p), a, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of ep_layout_dispatch_noalloc: the layout workspace (column totals
+// and chunk tables) of one call, in the library's own device memory so that
+// the call allocates nothing.  Each device holds its own copy for the life of
+// the process.  In host code `scratch` is only a stand-in for the symbol:
+// kernels get the device address that hipGetSymbolAddress returns, never
+// the array's name.
+static __device__ __align__(256) unsigned char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.  The stream must belong to the
+// current device, since the kernels run there.
+int device_scratch(hipStream_t stream, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return EP_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return EP_ERR_HIP;
+        if (sdev != dev) return EP_ERR_INVALID_ARG;
+    }
+    void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        ptr = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return EP_ERR_HIP;
+            g_scratch[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout_dispatch_noalloc(const ep_problem *p, const int32_t *topk_idx, int32_t *expert_count,
+                               int32_t *expert_offset, int32_t *rank_row_count,
+                               int32_t *rank_token_count, int32_t *group_token_count,
+                               uint8_t *is_token_in_rank, int32_t *token_slot,
+                               int64_t *cumulative_expert_recv, int32_t *status, const uint16_t *x,
+                               const float *topk_weights, uint16_t *recv_x, int32_t *recv_src_token,
+                               float *recv_weight, void *stream) {
+    // sizes first, so that a problem too large for the scratch is refused
+    // before any device call
+    int rc = check_problem(p);
+    if (rc != EP_OK) return rc;
+    const WsLayout w = epget::ws_layout(p->num_tokens, p->num_topk, p->num_experts,
+                                        p->num_ranks, p->num_groups);
+    if (w.bytes > static_cast<int64_t>(EP_NOALLOC_SCRATCH_BYTES)) return EP_ERR_SCRATCH_LIMIT;
+    if (!status || !aligned(status, 4)) return EP_ERR_INVALID_ARG;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if ((rc = device_scratch(st, &ws)) != EP_OK) return rc;
+    epget::LayoutParams lp;
+    rc = layout_params(p, topk_idx, expert_count, expert_offset, rank_row_count, rank_token_count,
+                       group_token_count, is_token_in_rank, token_slot, cumulative_expert_recv, ws,
+                       EP_NOALLOC_SCRATCH_BYTES, &lp);
+    if (rc != EP_OK) return rc;
+    lp.status = status;  // the caller's word, not the scratch's first bytes
+    epget::DispatchArgs a = {};
+    if (p->num_tokens > 0) {
+        rc = dispatch_args(x, topk_weights, token_slot, recv_x, recv_src_token, recv_weight, &a);
+        if (rc != EP_OK) return rc;
+    }
+    return hip_rc(epget::launch_layout_dispatch(lp, copy_params(p), a, st));
+}
+
 int ep_quantize_fp8(const ep_problem *p, const uint16_t *x, uint8_t *x_fp8, float *x_sf,
                     void *stream) {
     int rc = check_shape(p);
@@ -421,6 +501,8 @@ const char *ep_error_string(int code) {
         case EP_ERR_HIP: return "HIP runtime error";
         case EP_ERR_CAPACITY: return "rank slice capacity exceeded";
         case EP_ERR_BAD_EXPERT: return "expert id out of range";
+        case EP_ERR_SCRATCH_LIMIT:
+            return "problem needs more layout scratch than the library's static buffer holds";
         default: return "unknown error";
     }
 }

@@ -58,7 +58,11 @@ extern "C" {
 #define EP_ERR_HIP (-2)         /* a HIP runtime call or kernel launch failed */
 #define EP_ERR_CAPACITY (-3)    /* some rank needs more than S rows (device-detected) */
 #define EP_ERR_BAD_EXPERT (-4)  /* an id outside [0,E) other than -1 (device-detected) */
+#define EP_ERR_SCRATCH_LIMIT (-5) /* the problem needs more than EP_NOALLOC_SCRATCH_BYTES of
+                                     layout scratch (ep_layout_dispatch_noalloc only) */
 
+/* Size of the static device buffer behind ep_layout_dispatch_noalloc. */
+#define EP_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /* Limits of [V2] (kNumMaxRanks, kNumMaxExperts, kNumMaxExpertsPerRank)
  * and this library's own top-k and hidden-size limits (a row of H bf16
@@ -191,6 +195,36 @@ int ep_layout_dispatch(const ep_problem *problem, const int32_t *topk_idx,
                        const uint16_t *x, const float *topk_weights,
                        uint16_t *recv_x, int32_t *recv_src_token,
                        float *recv_weight, void *stream);
+
+/* ep_layout_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The layout's scratch lives in a static
+ * device array of EP_NOALLOC_SCRATCH_BYTES (8 MiB) inside the library, one
+ * copy per device, held until the process ends; the call itself allocates
+ * and frees nothing.  The status word goes to the caller's `status` (one
+ * int32, device, 4-byte aligned; read it with ep_read_status(status,
+ * stream)); every other argument, output, error and status is that of
+ * ep_layout_dispatch, and the results are identical.
+ *
+ * Limits: a problem whose workspace (ep_workspace_bytes) exceeds
+ * EP_NOALLOC_SCRATCH_BYTES is refused with EP_ERR_SCRATCH_LIMIT before
+ * anything is enqueued.  That covers, e.g., 128 chunks of 1024 entries at
+ * the largest E, R and G, and over two million entries at E = 256, R = 16.
+ * The scratch of the current device is used, and the stream must belong to
+ * that device (else EP_ERR_INVALID_ARG).  Every call on a device shares that
+ * device's scratch: calls that overlap on one device (on different streams,
+ * or from different host threads without ordering) race and give wrong
+ * results.  Calls in order on one stream are safe; the scratch keeps the
+ * last call's contents, and each call rewrites what it reads, so nothing
+ * needs clearing between calls. */
+int ep_layout_dispatch_noalloc(const ep_problem *problem, const int32_t *topk_idx,
+                               int32_t *expert_count, int32_t *expert_offset,
+                               int32_t *rank_row_count, int32_t *rank_token_count,
+                               int32_t *group_token_count, uint8_t *is_token_in_rank,
+                               int32_t *token_slot, int64_t *cumulative_expert_recv,
+                               int32_t *status, const uint16_t *x, const float *topk_weights,
+                               uint16_t *recv_x, int32_t *recv_src_token, float *recv_weight,
+                               void *stream);
 
 /* Combine: out[t,h] = bf16(sum_{j<K} w[t,j] * y[token_slot[t,j], h]), with an
  * fp32 accumulator folded in ascending j by fused multiply-add and one

@@ -84,6 +84,24 @@ def test_count_table_limit():
     assert ep.ep_workspace_bytes(P(T=258111 * 32 + 1, K=32, **big)) == 0
 
 
+def test_noalloc_scratch_limit_refused_on_host():
+    """ep_layout_dispatch_noalloc refuses a problem whose layout workspace
+    exceeds the static scratch before any device call (so this runs without
+    a GPU): large16k fits, a batch sixteen times larger at E = 2048 does not."""
+    lib = ep.load()
+    fake = 1 << 20   # never dereferenced
+    ok = P(T=16384, R=16, G=2)
+    assert ep.ep_workspace_bytes(ok) <= ep.EP_NOALLOC_SCRATCH_BYTES
+    big = P(T=16384 * 16, E=2048, R=1024, G=1024, S=1)
+    assert ep.ep_workspace_bytes(big) > ep.EP_NOALLOC_SCRATCH_BYTES
+    rc = lib.ep_layout_dispatch_noalloc(ctypes.byref(big), *([fake] * 15), None)
+    assert rc == ep.EP_ERR_SCRATCH_LIMIT
+    assert "scratch" in ep.error_string(rc)
+    # invalid problems are still invalid arguments
+    rc = lib.ep_layout_dispatch_noalloc(ctypes.byref(P(K=0)), *([fake] * 15), None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+
+
 def test_reserved_field_must_be_zero():
     p = P()
     p.reserved = 1
