@@ -8,6 +8,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libepget.so")
 SOURCES = ["api.hip", "layout.hip", "rows.hip", "hier.hip"]
+# bandwidth probes the benchmark compares the kernels with (not the path)
+PROBE_LIB = os.path.join(HERE, "libepprobe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,17 +25,23 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libepget.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _compile(lib: str, sources, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in sources]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libepget.so and the probe library libepprobe.so (always
+    recompiles both)."""
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":
