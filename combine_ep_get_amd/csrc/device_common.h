@@ -64,7 +64,13 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // store_token_rows: the vectors to the K destination rows (a row outside
 // [0, num_rows) is skipped); with `meta`, also each received row's source
 // token and weight and its scale factors.  lane_slot as for slot_of.
-template <int VPT, int NT = kCopyThreads>
+// kStream stores the rows with the non-temporal hint, for batches whose rows
+// all fit in the caches: plain stores leave them dirty in L2, and the
+// write-back at the end of the kernel then delays its completion (a
+// 128-token decode step took 9.3 µs with plain stores and 8.7-8.9 µs with
+// streaming ones, while a 16384-token step lost 5 %: there the rows leave L2
+// during the kernel anyway, and streaming stores reach HBM more slowly).
+template <int VPT, int NT = kCopyThreads, bool kStream = false>
 __device__ __forceinline__ void store_token_rows(const CopyParams &c, const DispatchArgs &a, int t, int v0,
                                                  bool meta, int32_t lane_slot, const u32x4 (&buf)[VPT]) {
     if (meta) {
@@ -94,7 +100,12 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int col = v0 + v * NT;
-            if (col < c.nvec) dst[col] = buf[v];
+            if (col < c.nvec) {
+                if (kStream)
+                    __builtin_nontemporal_store(buf[v], dst + col);
+                else
+                    dst[col] = buf[v];
+            }
         }
         if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }

@@ -110,8 +110,11 @@ hipError_t launch_combine_weights(const CopyParams &c, const float *recv_w, cons
 
 // Grid shape for the row kernels with workgroups of `threads`: (tokens,
 // column splits) and vectors per thread, chosen so that small batches still
-// spread over all CUs.
-void copy_grid(int32_t T, int32_t nvec, int32_t threads, int32_t *splits, int32_t *vpt);
+// spread over about `want` workgroups.
+constexpr int kCopyWorkgroups = 2048;   // 8 per CU
+constexpr int kFusedWorkgroups = 1024;  // the single-kernel layout + dispatch
+void copy_grid(int32_t T, int32_t nvec, int32_t threads, int32_t *splits, int32_t *vpt,
+               int32_t want = kCopyWorkgroups);
 // Grid of the combine: (tokens, row pieces) and threads per workgroup (one
 // 16-byte column vector per thread).
 void combine_grid(int32_t T, int32_t nvec, int32_t *splits, int32_t *threads);

@@ -846,7 +846,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutPa
     const bool meta = blockIdx.y == 1;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
-    store_token_rows<VPT, kFusedThreads>(c, a, t, v0, meta, lane_slot, buf);
+    store_token_rows<VPT, kFusedThreads, true>(c, a, t, v0, meta, lane_slot, buf);
 }
 
 // Largest chunk count of the two-launch one-call path: a wave reads the
@@ -1062,8 +1062,13 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
     // stays ahead (16.4 against 26.8 µs at T = 200, R = 256).
     const bool one_chunk = p.T > 0 && static_cast<int64_t>(p.T) * p.K <= kFusedMaxEntries &&
                            (p.nchunks <= 3 || p.R <= 64);
+    // The single kernel aims at half the copy kernels' workgroups: each of
+    // them builds the batch's histograms, and at 512 tokens 1024 workgroups
+    // took the step from 29.9 to 26.7 µs against 2048 (at 128 tokens a row
+    // has only four workgroups' worth of vectors either way).
     int32_t splits, vpt;
-    copy_grid(c.T, c.nvec, one_chunk ? kFusedThreads : kCopyThreads, &splits, &vpt);
+    copy_grid(c.T, c.nvec, one_chunk ? kFusedThreads : kCopyThreads, &splits, &vpt,
+              one_chunk ? kFusedWorkgroups : kCopyWorkgroups);
     CopyParams cp = c;
     cp.vpt = vpt;
     const dim3 grid(c.T, splits + 1);

@@ -225,11 +225,11 @@ __global__ __launch_bounds__(256) void combine_weights_kernel(CopyParams c, cons
 
 }  // namespace
 
-void copy_grid(int32_t T, int32_t nvec, int32_t threads, int32_t *splits, int32_t *vpt) {
-    // Aim for at least ~2048 workgroups (8 per CU) so that decode-sized
-    // batches still cover the chip; large batches get one workgroup per token
-    // and several vectors per thread.
-    const int64_t want_blocks = 2048;
+void copy_grid(int32_t T, int32_t nvec, int32_t threads, int32_t *splits, int32_t *vpt, int32_t want) {
+    // Aim for at least `want` workgroups so that decode-sized batches still
+    // cover the chip; large batches get one workgroup per token and several
+    // vectors per thread.
+    const int64_t want_blocks = want;
     int64_t need = T >= want_blocks ? 1 : (want_blocks + (T > 0 ? T : 1) - 1) / (T > 0 ? T : 1);
     int64_t v = (nvec + threads * need - 1) / (threads * need);
     if (v < 1) v = 1;
