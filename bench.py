@@ -258,6 +258,7 @@ def probe_lib():
     lib.ep_probe_copy.argtypes = [vp, vp, i64, vp]
     lib.ep_probe_gather.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     lib.ep_probe_scatter.argtypes = [vp, vp, i64, ctypes.c_int, vp]
+    lib.ep_probe_empty.argtypes = [vp]
     return lib
 
 
@@ -299,6 +300,10 @@ def ceilings(torch, nbytes=PROBE_BYTES, iters=20):
     for name, (fn, ways) in probes.items():
         ms = _time_ms(torch, stream, fn, iters)
         out[name + "_gbps"] = ways * nbytes / (ms * 1e-3) / 1e9
+    # launch-to-launch floor of the stream: an empty one-workgroup kernel
+    # back to back (what a latency-bound step of n kernels cannot go below n
+    # times)
+    out["empty_kernel_us"] = 1e3 * _time_ms(torch, stream, lambda: call(lib.ep_probe_empty(st)), 200)
     out["gather8_scatter8_note"] = ("gather8: 8 planes of 128 MiB folded into one (the combine's "
                                    "8 : 1 reads to writes); scatter8: one plane stored to 8 (the "
                                    "dispatch's 1 : 8)")

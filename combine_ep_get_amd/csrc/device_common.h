@@ -63,35 +63,29 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 // store_token_rows: the vectors to the K destination rows (a row outside
 // [0, num_rows) is skipped); with `meta`, also each received row's source
-// token and weight and its scale factors.  lane_slot as for slot_of.
+// token and weight and its scale factors.  lane_slot as for slot_of.  The
+// weight is loaded where it is written, and its wait holds back what
+// follows: with kMetaLast the source and weight go after the rows, otherwise
+// before them (measured: after the rows, the 16384-token one-call step took
+// 769 µs against 772; before them, the 128-token decode step 8.7 µs against
+// 9.1).  Scale factors always go after the rows.
 // kStream stores the rows with the non-temporal hint, for batches whose rows
 // all fit in the caches: plain stores leave them dirty in L2, and the
 // write-back at the end of the kernel then delays its completion (a
 // 128-token decode step took 9.3 µs with plain stores and 8.7-8.9 µs with
 // streaming ones, while a 16384-token step lost 5 %: there the rows leave L2
 // during the kernel anyway, and streaming stores reach HBM more slowly).
-template <int VPT, int NT = kCopyThreads, bool kStream = false>
+template <int VPT, int NT = kCopyThreads, bool kStream = false, bool kMetaLast = false>
 __device__ __forceinline__ void store_token_rows(const CopyParams &c, const DispatchArgs &a, int t, int v0,
                                                  bool meta, int32_t lane_slot, const u32x4 (&buf)[VPT]) {
-    if (meta) {
-        if (static_cast<int>(threadIdx.x) < c.K) {
-            const int j = threadIdx.x;  // lane j of wave 0
-            if (slot_ok(lane_slot, c.num_rows)) {
-                if (a.recv_src) a.recv_src[lane_slot] = t;
-                if (a.recv_w) a.recv_w[lane_slot] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
-            }
-        }
-        // per-row scale factors, one thread per block of channels
-        if (a.x_sf) {
-            for (int b = threadIdx.x; b < a.nsf; b += NT) {
-                const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
-                for (int j = 0; j < c.K; ++j) {
-                    const int32_t s = slot_of(lane_slot, j);
-                    if (slot_ok(s, c.num_rows)) a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
-                }
-            }
-        }
-    }
+    // lane j of wave 0 writes entry j's source and weight (j < K)
+    const bool meta_lane = meta && static_cast<int>(threadIdx.x) < c.K && slot_ok(lane_slot, c.num_rows);
+    auto write_meta = [&] {
+        const int j = threadIdx.x;
+        if (a.recv_src) a.recv_src[lane_slot] = t;
+        if (a.recv_w) a.recv_w[lane_slot] = a.w ? a.w[static_cast<int64_t>(t) * c.K + j] : 1.0f;
+    };
+    if (!kMetaLast && meta_lane) write_meta();
     u32x4 *recv = static_cast<u32x4 *>(a.recv);
     for (int j = 0; j < c.K; ++j) {
         const int32_t s = slot_of(lane_slot, j);
@@ -108,6 +102,18 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
             }
         }
         if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    if (kMetaLast && meta_lane) write_meta();
+    // per-row scale factors, one thread per block of channels, after the
+    // rows so that their loads do not hold the rows' stores back
+    if (meta && a.x_sf) {
+        for (int b = threadIdx.x; b < a.nsf; b += NT) {
+            const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
+            for (int j = 0; j < c.K; ++j) {
+                const int32_t s = slot_of(lane_slot, j);
+                if (slot_ok(s, c.num_rows)) a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
+            }
+        }
     }
 }
 

@@ -849,6 +849,24 @@ __global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutPa
     store_token_rows<VPT, kFusedThreads, true>(c, a, t, v0, meta, lane_slot, buf);
 }
 
+// Workgroups that lead the 1-D grid of the multi-chunk one-call kernel:
+// the first takes the layout outputs, the others have nothing to do.  Eight
+// keep the copy workgroups on the XCDs (linear id modulo 8) that the
+// combine's grid gives the same tokens.  A (T, splits + 1) grid with the
+// layout in row 0 left T - 1 workgroups idle, all dispatched ahead of the
+// copies: 16383 of them at 16384 tokens, where the 1-D grid took the step
+// from 772 to 769 µs.  (The decode-sized kernel keeps its 2-D grid, which
+// measured 0.3 µs faster on a 128-token step.)
+constexpr int kLeadWorkgroups = 8;
+
+// Token and column run of copy workgroup `b` (b >= kLeadWorkgroups) of a
+// grid of kLeadWorkgroups + T * splits workgroups.
+__device__ __forceinline__ void copy_role(int b, int T, int *t, int *run) {
+    const int i = b - kLeadWorkgroups;
+    *run = i / T;
+    *t = i - *run * T;
+}
+
 // Largest chunk count of the two-launch one-call path: a wave reads the
 // per-chunk counts with one lane per chunk, in CR <= kMaxChunkRounds rounds
 // of 64 chunks.
@@ -995,21 +1013,24 @@ __device__ void finish_layout_from_table(const LayoutParams &p, int *lds) {
 }
 
 // Layout and dispatch of a multi-chunk batch (A = 1, at most kMaxCallChunks
-// chunks) in the launch after the count pass, on a (T, splits + 1) grid:
-// workgroup (0, 0) writes the layout outputs from the table, the rest of row
-// y = 0 has nothing to do, and workgroup (t, y > 0) derives token t's slots,
-// writes them if y == 1, and dispatches column run y - 1 of its row.
+// chunks) in the launch after the count pass, on a 1-D grid of
+// kLeadWorkgroups + T * splits workgroups: workgroup 0 writes the layout
+// outputs from the table, and copy workgroup (t, run) derives token t's
+// slots, writes them if run == 0, and dispatches column run `run` of its
+// row.
 template <int VPT, int CR>
 __global__ __launch_bounds__(kCopyThreads) void dispatch_chunks_kernel(LayoutParams p, CopyParams c,
                                                                        DispatchArgs a) {
     extern __shared__ __align__(16) int smem[];
     __shared__ int s_part[EP_MAX_TOPK];
-    if (blockIdx.y == 0) {
-        if (blockIdx.x == 0) finish_layout_from_table<kCopyThreads>(p, smem);
+    const int b = blockIdx.x;
+    if (b < kLeadWorkgroups) {
+        if (b == 0) finish_layout_from_table<kCopyThreads>(p, smem);
         return;
     }
-    const int t = blockIdx.x;
-    const int v0 = (blockIdx.y - 1) * (kCopyThreads * VPT) + threadIdx.x;
+    int t, run;
+    copy_role(b, p.T, &t, &run);
+    const int v0 = run * (kCopyThreads * VPT) + threadIdx.x;
     u32x4 buf[VPT];
     // early sums pay when the kernel still fits 64 VGPRs (16 workgroups per
     // CU) or when a batch of more than 64 chunks needs several rounds of
@@ -1017,10 +1038,10 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_chunks_kernel(LayoutPar
     constexpr bool kEarlySums = CR > 1 || VPT <= 4;
     const int32_t lane_slot = token_slots_in_chunk<kCopyThreads, CR, kEarlySums>(
         p, t, t / p.chunk_tokens, smem, s_part, [&] { load_token_row<VPT>(c, a, t, v0, buf); });
-    const bool meta = blockIdx.y == 1;
+    const bool meta = run == 0;
     if (meta && static_cast<int>(threadIdx.x) < p.K)
         p.token_slot[static_cast<int64_t>(t) * p.K + threadIdx.x] = lane_slot;
-    store_token_rows<VPT>(c, a, t, v0, meta, lane_slot, buf);
+    store_token_rows<VPT, kCopyThreads, false, true>(c, a, t, v0, meta, lane_slot, buf);
 }
 
 }  // namespace
@@ -1071,8 +1092,10 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
               one_chunk ? kFusedWorkgroups : kCopyWorkgroups);
     CopyParams cp = c;
     cp.vpt = vpt;
-    const dim3 grid(c.T, splits + 1);
     if (!one_chunk && p.T > 0 && p.nchunks <= kMaxCallChunks && p.A == 1) {
+        const int64_t blocks = kLeadWorkgroups + static_cast<int64_t>(c.T) * splits;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        const dim3 grid(static_cast<uint32_t>(blocks));
         // count pass (with the expert-major arrays), then one launch that
         // finishes the layout and dispatches, each workgroup deriving its
         // token's slots
@@ -1109,6 +1132,7 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
         if (err != hipSuccess || p.T == 0) return err;
         return launch_dispatch(c, a, stream);
     }
+    const dim3 grid(c.T, splits + 1);
     // LDS: the larger of the layout workgroup's (ids, histogram, aligned
     // scan) and a dispatch workgroup's (two histograms and a scan)
     const size_t lds = sizeof(int) * std::max<size_t>(kChunkEntries + p.pitch + p.E + 1,

@@ -102,6 +102,10 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const u32x4 *__restri
     for (int p = 0; p < k; ++p) dst[static_cast<int64_t>(p) * n + i] = v;
 }
 
+// One workgroup that does nothing: back to back, the launch-to-launch floor
+// of a stream, against which latency-bound steps of a few kernels are read.
+__global__ __launch_bounds__(64) void empty_kernel() {}
+
 // Grid for n vectors; 0 if the size is not usable (n < 1 or too many tiles).
 uint32_t grid_for(int64_t bytes) {
     if (bytes < 16 || bytes % 16 != 0) return 0;
@@ -148,6 +152,11 @@ int ep_probe_copy(const void *src, void *dst, int64_t bytes, void *stream) {
         return -1;
     copy_kernel<<<g, kThreads, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4 *>(src),
                                                                         static_cast<u32x4 *>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int ep_probe_empty(void *stream) {
+    empty_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>();
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
