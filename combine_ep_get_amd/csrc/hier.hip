@@ -108,18 +108,108 @@ __global__ __launch_bounds__(NT) void group_layout_kernel(int32_t T, int32_t R, 
 
 // Group slots of a batch of more than 4096 tokens: tiles of kTileTokens
 // tokens, one workgroup per (tile, group), all running at once.  A
-// workgroup counts the tokens of the earlier tiles that reach its group
-// (reading their rank bytes again, four tokens per thread in flight, together
-// with its own tile's), then places its own tile as one pass of
-// group_layout_kernel does (two flags per thread).  The recount costs each workgroup one read of the earlier part of
-// the map, which stays in cache; a single workgroup per group walked the
-// batch pass after pass, each pass paying the map's load latency on one CU.
+// workgroup finds how many tokens of the earlier tiles reach its group, then
+// places its own tile as one pass of group_layout_kernel does (two flags per
+// thread).  Two ways to find the earlier tiles' count:
+//   - kPrefixed: three launches.  group_tile_count_kernel writes each
+//     (tile, group) count into the group slot of the tile's first token,
+//     group_tile_scan_kernel turns those counts into exclusive prefixes in
+//     place, and each placing workgroup reads its own tile's prefix before
+//     it overwrites the tile; no workgroup reads a slot another one writes.
+//   - otherwise one launch, in which each workgroup recounts the earlier
+//     tiles (reading their rank bytes again, four tokens per thread in
+//     flight, together with its own tile's).  The recount grows with the
+//     square of the batch: the last tile's workgroup reads nearly the whole
+//     map.
+// A single workgroup per group walking the batch pass after pass paid the
+// map's load latency on one CU at every pass.
 constexpr int kTileThreads = 1024;
 constexpr int kTileTpt = 2;
 constexpr int kRecountTpt = 4;
 constexpr int kTileTokens = kTileThreads * kTileTpt;
 
+// Smallest tile count that takes the three launches.  Measured (µs, R = 16,
+// G = 2): recount 6.2 at 4 tiles, 9.5 at 8, 30.2 at 32; three launches
+// 8.2-8.8 at any size up to 64 tiles (and at R = 1024, G = 128, 32768
+// tokens: 84 against 418).
+constexpr int kPrefixMinTiles = 7;
+
+// Whether token t reaches group g, for the kTileTpt tokens base + i + k *
+// kTileThreads of a tile (tokens past T give 0).
 template <bool kWords>
+__device__ __forceinline__ void tile_flags(int32_t T, int32_t R, const HierParams &h, const uint8_t *map, int g,
+                                           int base, uint32_t (&in)[kTileTpt]) {
+    const int i = threadIdx.x, r0 = g * h.ranks_per_group;
+#pragma unroll
+    for (int k = 0; k < kTileTpt; ++k) in[k] = 0;
+    for (int r = 0; r < h.ranks_per_group; r += kWords ? 4 : 1) {
+#pragma unroll
+        for (int k = 0; k < kTileTpt; ++k) {
+            const int t = min(base + i + k * kTileThreads, T - 1);
+            const uint8_t *b = map + static_cast<int64_t>(t) * R + r0 + r;
+            in[k] |= kWords ? *reinterpret_cast<const uint32_t *>(b) : *b;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kTileTpt; ++k) in[k] = (base + i + k * kTileThreads < T && in[k]) ? 1u : 0u;
+}
+
+// Pass 1 of the three-launch form: tokens of tile blockIdx.x reaching group
+// blockIdx.y, written to group_slot[first token of the tile, g].
+template <bool kWords>
+__global__ __launch_bounds__(kTileThreads) void group_tile_count_kernel(int32_t T, int32_t R, HierParams h,
+                                                                        const uint8_t *__restrict__ map,
+                                                                        int32_t *__restrict__ group_slot) {
+    __shared__ int s_wsum[kTileThreads / 64];
+    const int c = blockIdx.x, g = blockIdx.y;
+    const int i = threadIdx.x, lane = __lane_id(), w = i >> 6;
+    const int base = c * kTileTokens;
+    uint32_t in[kTileTpt];
+    tile_flags<kWords>(T, R, h, map, g, base, in);
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < kTileTpt; ++k) n += static_cast<int>(in[k]);
+    const int incl = wave_inclusive_sum(n);
+    if (lane == 63) s_wsum[w] = incl;
+    __syncthreads();
+    if (i == 0) {
+        int total = 0;
+#pragma unroll
+        for (int q = 0; q < kTileThreads / 64; ++q) total += s_wsum[q];
+        group_slot[static_cast<int64_t>(base) * h.G + g] = total;
+    }
+}
+
+// Pass 2: for group blockIdx.x, the tile counts left by pass 1 (in the slot
+// of each tile's first token) become exclusive prefixes, in place, 1024
+// tiles at a time.  (Pass 3's last tile reports an overflow.)
+__global__ __launch_bounds__(kTileThreads) void group_tile_scan_kernel(int32_t ntiles, HierParams h,
+                                                                       int32_t *__restrict__ group_slot) {
+    __shared__ int s_wsum[kTileThreads / 64];
+    const int g = blockIdx.x;
+    const int i = threadIdx.x, lane = __lane_id(), w = i >> 6;
+    int carry = 0;
+    for (int c0 = 0; c0 < ntiles; c0 += kTileThreads) {
+        const int c = c0 + i;
+        int32_t *at = group_slot + (static_cast<int64_t>(min(c, ntiles - 1)) * kTileTokens) * h.G + g;
+        const int v = c < ntiles ? *at : 0;
+        const int incl = wave_inclusive_sum(v);
+        if (lane == 63) s_wsum[w] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int q = 0; q < kTileThreads / 64; ++q) {
+            const int s = s_wsum[q];
+            before += q < w ? s : 0;
+            total += s;
+        }
+        if (c < ntiles) *at = carry + before + incl - v;
+        carry += total;
+        __syncthreads();  // s_wsum is rewritten by the next round
+    }
+}
+
+template <bool kWords, bool kPrefixed>
 __global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, int32_t R, HierParams h,
                                                                    const uint8_t *__restrict__ map,
                                                                    int32_t *__restrict__ group_slot,
@@ -128,27 +218,22 @@ __global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, in
     __shared__ int s_first[kTileThreads];
     __shared__ uint32_t s_bits[kTileThreads];
     __shared__ int s_wsum[kTileThreads / 64];
+    __shared__ int s_prefix;
     const int c = blockIdx.x, g = blockIdx.y;
     const int i = threadIdx.x, lane = __lane_id(), w = i >> 6;
     const int r0 = g * h.ranks_per_group;
     const int base = c * kTileTokens;
+    // the prefix the scan left in the slot of the tile's first token, read
+    // before any thread of this workgroup overwrites it
+    if (kPrefixed && i == 0) s_prefix = group_slot[static_cast<int64_t>(base) * h.G + g];
     // the tile's own rank bytes first, so that their loads are in flight
     // with the recount's
     uint32_t in_tile[kTileTpt];
-#pragma unroll
-    for (int k = 0; k < kTileTpt; ++k) in_tile[k] = 0;
-    for (int r = 0; r < h.ranks_per_group; r += kWords ? 4 : 1) {
-#pragma unroll
-        for (int k = 0; k < kTileTpt; ++k) {
-            const int t = min(base + i + k * kTileThreads, T - 1);
-            const uint8_t *b = map + static_cast<int64_t>(t) * R + r0 + r;
-            in_tile[k] |= kWords ? *reinterpret_cast<const uint32_t *>(b) : *b;
-        }
-    }
+    tile_flags<kWords>(T, R, h, map, g, base, in_tile);
     // 1. tokens before the tile that reach the group, kRecountTpt per thread
-    // in flight
+    // in flight (without a prefix)
     int cnt = 0;
-    for (int t0 = i; t0 < base; t0 += kRecountTpt * kTileThreads) {
+    for (int t0 = i; !kPrefixed && t0 < base; t0 += kRecountTpt * kTileThreads) {
         uint32_t in[kRecountTpt];
 #pragma unroll
         for (int k = 0; k < kRecountTpt; ++k) in[k] = 0;
@@ -168,12 +253,15 @@ __global__ __launch_bounds__(kTileThreads) void group_tiles_kernel(int32_t T, in
     if (lane == 63) s_wsum[w] = cnt_incl;
     // 2. the tile: flags in token order, kTileTpt consecutive flags per thread
 #pragma unroll
-    for (int k = 0; k < kTileTpt; ++k)
-        s_flag[i + k * kTileThreads] = (base + i + k * kTileThreads < T && in_tile[k]) ? 1 : 0;
+    for (int k = 0; k < kTileTpt; ++k) s_flag[i + k * kTileThreads] = static_cast<uint8_t>(in_tile[k]);
     __syncthreads();
     int carry = 0;
+    if (kPrefixed) {
+        carry = s_prefix;
+    } else {
 #pragma unroll
-    for (int q = 0; q < kTileThreads / 64; ++q) carry += s_wsum[q];
+        for (int q = 0; q < kTileThreads / 64; ++q) carry += s_wsum[q];
+    }
     __syncthreads();
     uint32_t bits = 0;
 #pragma unroll
@@ -213,8 +301,15 @@ void launch_group_layout_nt(int32_t T, int32_t R, const HierParams &h, const uin
     } else if (T <= 256 * kGroupTpt) {
         group_layout_kernel<kWords, 256><<<h.G, 256, 0, stream>>>(T, R, h, map, group_slot, status);
     } else {
-        const dim3 grid((T + kTileTokens - 1) / kTileTokens, h.G);
-        group_tiles_kernel<kWords><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot, status);
+        const int ntiles = (T + kTileTokens - 1) / kTileTokens;
+        const dim3 grid(ntiles, h.G);
+        if (ntiles >= kPrefixMinTiles) {
+            group_tile_count_kernel<kWords><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot);
+            group_tile_scan_kernel<<<h.G, kTileThreads, 0, stream>>>(ntiles, h, group_slot);
+            group_tiles_kernel<kWords, true><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot, status);
+        } else {
+            group_tiles_kernel<kWords, false><<<grid, kTileThreads, 0, stream>>>(T, R, h, map, group_slot, status);
+        }
     }
 }
 

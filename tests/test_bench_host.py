@@ -82,3 +82,24 @@ def test_write_traffic_calibrates_on_probes(tmp_path, monkeypatch):
     assert "large16k" in saved["workloads"]
     # the record is used while the sources are unchanged
     assert bench.measured_traffic("large16k", "combine") == pytest.approx(17000 * 1024)
+
+
+def test_probe_library_exports_and_refuses_bad_sizes():
+    """libepprobe.so (the ceilings' probe kernels) loads, lists its gather and
+    scatter shapes, and refuses bad sizes before launching anything."""
+    import ctypes
+
+    lib = bench.probe_lib()
+    for name in ("ep_probe_read", "ep_probe_write", "ep_probe_copy", "ep_probe_mix", "ep_probe_mix_shapes",
+                 "ep_probe_mix_shape", "ep_probe_empty"):
+        assert hasattr(lib, name), name
+    assert lib.ep_probe_mix_shapes(0) == 6 and lib.ep_probe_mix_shapes(1) == 7
+    v, nt, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.ep_probe_mix_shape(1, 4, ctypes.byref(v), ctypes.byref(nt), ctypes.byref(w)) == 0
+    assert (v.value, nt.value, w.value) == (7, 128, 0)
+    assert lib.ep_probe_mix_shape(0, 6, ctypes.byref(v), ctypes.byref(nt), ctypes.byref(w)) == -1
+    fake = 1 << 20   # never dereferenced: the size checks come first
+    assert lib.ep_probe_read(fake, 0, 0, fake, None) == -1
+    assert lib.ep_probe_write(fake, 24, 0, None) == -1
+    assert lib.ep_probe_copy(fake, fake + 8, 1 << 20, None) == -1    # misaligned
+    assert lib.ep_probe_mix(0, 0, fake, fake, 8, None) == -1
