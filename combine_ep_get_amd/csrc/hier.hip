@@ -351,9 +351,28 @@ __device__ __forceinline__ void for_each_group_row(const HierParams &h, const in
     }
 }
 
+// Whether a batch's group rows are too many for the 256 MB last-level cache
+// to hold them between two stages: the estimate is min(G, K) rows per token.
+// Past 192 MiB the stages that write group rows (the dispatch's first, the
+// combine's partials) store them with the non-temporal hint; below it
+// plainly, so that the next stage finds them in the cache.  Two-level steps
+// (H = 7168, G = 2; µs, plain → non-temporal, group rows by the estimate):
+//   T = 4096, R = 8 (117 MB)     278.4 → 287.5
+//   T = 6144, R = 16 (176 MB)    418.7 → 422.0
+//   T = 9000, R = 16 (258 MB)    632.9 → 610.6
+//   T = 12000, R = 16 (344 MB)   860.2 → 811.4
+//   T = 16384, R = 16 (470 MB)  1171.5 → 1106.7
+// and the 8192-token Zipf batch with 8 KB rows (134 MB) 301.3 → 309.6.
+constexpr int64_t kGroupStreamBytes = int64_t(192) << 20;
+
+bool stream_group_rows(const CopyParams &c, const HierParams &h) {
+    const int64_t per_token = h.G < c.K ? h.G : c.K;
+    return static_cast<int64_t>(c.T) * per_token * c.nvec * 16 > kGroupStreamBytes;
+}
+
 // Two-level dispatch, stage 1: token t's row, loaded once, to its row in
-// every group it reaches.
-template <int VPT, bool kWide>
+// every group it reaches (kStream: with the non-temporal hint).
+template <int VPT, bool kWide, bool kStream>
 __global__ __launch_bounds__(kCopyThreads) void group_dispatch_kernel(CopyParams c, HierParams h,
                                                                       const uint16_t *__restrict__ x,
                                                                       const int32_t *__restrict__ group_slot,
@@ -370,7 +389,11 @@ __global__ __launch_bounds__(kCopyThreads) void group_dispatch_kernel(CopyParams
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const int col = v0 + v * kCopyThreads;
-            if (col < c.nvec) dst[col] = buf[v];
+            if (col >= c.nvec) continue;
+            if constexpr (kStream)
+                __builtin_nontemporal_store(buf[v], dst + col);
+            else
+                dst[col] = buf[v];
         }
         if (VPT >= kRowWaitMinVpt) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     });
@@ -383,7 +406,8 @@ __global__ __launch_bounds__(kCopyThreads) void group_dispatch_kernel(CopyParams
 // gather_fold); gathering per group instead kept half as many loads in
 // flight and loaded row 0 for the other groups' entries: 18 µs slower on a
 // 4096-token step with four groups, 22 µs on 16384 tokens with two.
-template <int KG, bool kWide>
+// kStream stores the partials with the non-temporal hint.
+template <int KG, bool kWide, bool kStream>
 __global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
     CopyParams c, HierParams h, const uint16_t *__restrict__ y, const int32_t *__restrict__ slot,
     const float *__restrict__ w, const int32_t *__restrict__ group_slot,
@@ -395,6 +419,14 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
     const int colc = min(col, c.nvec - 1);
     const int32_t *gsrow = group_slot + static_cast<int64_t>(t) * h.G;
     u32x4 *rows = reinterpret_cast<u32x4 *>(group_buf);
+    auto store_partial = [&](int32_t gs, const float (&acc)[8]) {
+        if (col >= c.nvec) return;
+        u32x4 *dst = rows + static_cast<int64_t>(gs) * c.nvec + col;
+        if constexpr (kStream)
+            __builtin_nontemporal_store(pack_row(acc), dst);
+        else
+            *dst = pack_row(acc);
+    };
     if (c.K <= KG) {
         // all K rows in flight once, then folded group by group from registers
         u32x4 in[KG];
@@ -424,7 +456,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
                     acc[2 * q + 1] = grp[jj] == g ? hi : acc[2 * q + 1];
                 }
             }
-            if (col < c.nvec) rows[static_cast<int64_t>(gs) * c.nvec + col] = pack_row(acc);
+            store_partial(gs, acc);
         });
         return;
     }
@@ -433,7 +465,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_partial_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
         gather_fold<KG>(c, y, srow, wrow, colc, GroupOf{h.S, h.ranks_per_group, g}, acc);
-        if (col < c.nvec) rows[static_cast<int64_t>(gs) * c.nvec + col] = pack_row(acc);
+        store_partial(gs, acc);
     });
 }
 
@@ -606,13 +638,16 @@ hipError_t launch_group_dispatch(const CopyParams &c, const HierParams &h, const
     CopyParams p = c;
     p.vpt = vpt;
     dim3 grid(c.T, splits);
+    const bool stream_rows = stream_group_rows(c, h);
     switch (vpt) {
-#define EP_GROUP_DISPATCH_CASE(V)                                                                 \
-    case V:                                                                                       \
-        if (h.G > kNarrowGroups)                                                                  \
-            group_dispatch_kernel<V, true><<<grid, kCopyThreads, 0, stream>>>(p, h, x, group_slot, group_buf); \
-        else                                                                                      \
-            group_dispatch_kernel<V, false><<<grid, kCopyThreads, 0, stream>>>(p, h, x, group_slot, group_buf); \
+#define EP_GROUP_DISPATCH_KERNEL(V, W) \
+    (stream_rows ? group_dispatch_kernel<V, W, true> : group_dispatch_kernel<V, W, false>)
+#define EP_GROUP_DISPATCH_CASE(V)                                                                          \
+    case V:                                                                                                \
+        if (h.G > kNarrowGroups)                                                                           \
+            EP_GROUP_DISPATCH_KERNEL(V, true)<<<grid, kCopyThreads, 0, stream>>>(p, h, x, group_slot, group_buf); \
+        else                                                                                               \
+            EP_GROUP_DISPATCH_KERNEL(V, false)<<<grid, kCopyThreads, 0, stream>>>(p, h, x, group_slot, group_buf); \
         break;
         EP_GROUP_DISPATCH_CASE(1)
         EP_GROUP_DISPATCH_CASE(2)
@@ -623,6 +658,7 @@ hipError_t launch_group_dispatch(const CopyParams &c, const HierParams &h, const
         EP_GROUP_DISPATCH_CASE(7)
         EP_GROUP_DISPATCH_CASE(8)
 #undef EP_GROUP_DISPATCH_CASE
+#undef EP_GROUP_DISPATCH_KERNEL
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -661,15 +697,19 @@ hipError_t launch_combine_partial(const CopyParams &c, const HierParams &h, cons
     combine_grid(c.T, c.nvec, &splits, &threads);
     dim3 grid(c.T, splits);
     const bool wide = h.G > kNarrowGroups;
-    if (c.K <= 4 && wide) {
-        combine_partial_kernel<4, true><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
-    } else if (c.K <= 4) {
-        combine_partial_kernel<4, false><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
-    } else if (wide) {
-        combine_partial_kernel<8, true><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
-    } else {
-        combine_partial_kernel<8, false><<<grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf);
-    }
+    const bool stream_rows = stream_group_rows(c, h);
+#define EP_COMBINE_PARTIAL(KG, W)                                                                \
+    (stream_rows ? combine_partial_kernel<KG, W, true> : combine_partial_kernel<KG, W, false>)<<< \
+        grid, threads, 0, stream>>>(c, h, y, slot, w, group_slot, group_buf)
+    if (c.K <= 4 && wide)
+        EP_COMBINE_PARTIAL(4, true);
+    else if (c.K <= 4)
+        EP_COMBINE_PARTIAL(4, false);
+    else if (wide)
+        EP_COMBINE_PARTIAL(8, true);
+    else
+        EP_COMBINE_PARTIAL(8, false);
+#undef EP_COMBINE_PARTIAL
     return hipGetLastError();
 }
 
