@@ -345,10 +345,13 @@ class Bench:
         if args.fp8:
             nsf = wl.H // 128
             self.nsf = nsf
+            # received scale rows token-major, padded to whole 128-byte
+            # lines, which the dispatch then writes whole
+            self.sf_stride = -(-nsf // 32) * 32
             self.d_q = torch.empty((wl.T, wl.H), dtype=torch.uint8, device=dev)
             self.d_sf = torch.empty((wl.T, nsf), dtype=torch.float32, device=dev)
             self.recv_q = torch.empty((wl.R * S, wl.H), dtype=torch.uint8, device=dev)
-            self.recv_sf = torch.empty(wl.R * S * nsf, dtype=torch.float32, device=dev)
+            self.recv_sf = torch.empty(wl.R * S * self.sf_stride, dtype=torch.float32, device=dev)
             # quantisation happens upstream of dispatch (in the producing
             # layer); it is timed on its own and not part of the step
             self.quant_us = 1e3 * _time_ms(
@@ -375,7 +378,7 @@ class Bench:
         layout = [] if fused else [ep.ep_get_layout(p, self.d_idx, *bufs.args(), **b)]
         if fused and a.fp8:
             dispatch = [ep.ep_layout_dispatch_fp8(p, self.d_idx, *bufs.args(), None, self.d_q, self.d_sf,
-                                                  self.d_w, self.recv_q, self.recv_sf, self.nsf, 1,
+                                                  self.d_w, self.recv_q, self.recv_sf, self.sf_stride, 1,
                                                   self.recv_src, self.recv_w, **b)]
         elif fused:
             dispatch = [ep.ep_layout_dispatch(p, self.d_idx, *bufs.args(), None, self.d_x, self.d_w,
@@ -387,7 +390,7 @@ class Bench:
                                             self.gbuf, self.recv, self.recv_src, self.recv_w, **b)]
         elif a.fp8:
             dispatch = [ep.ep_dispatch_fp8(p, self.d_q, self.d_sf, self.d_w, bufs.token_slot, self.recv_q,
-                                           self.recv_sf, self.nsf, 1, self.recv_src, self.recv_w, **b)]
+                                           self.recv_sf, self.sf_stride, 1, self.recv_src, self.recv_w, **b)]
         else:
             dispatch = [ep.ep_dispatch(p, self.d_x, self.d_w, bufs.token_slot, self.recv, self.recv_src,
                                        self.recv_w, **b)]
@@ -652,6 +655,8 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "R": wl.R,
                    "G": b.p.num_groups, "A": wl.A, "S": b.S, "routing": wl.routing, "seed": wl.seed,
                    "dispatch": "fp8" if args.fp8 else "bf16",
+                   **({"recv_sf": f"token-major, rows of {b.sf_stride} floats (H/128 padded to 128-byte lines)"}
+                      if args.fp8 else {}),
                    "path": "two-level (group buffer)" if args.hier else "flat",
                    "layout_dispatch": ("one call (ep_layout_dispatch_fp8)" if args.fp8 else
                                        "one call (ep_layout_dispatch)") if fused else "two calls",

@@ -180,6 +180,10 @@ int dispatch_fp8_args(const ep_problem *p, const uint8_t *x_fp8, const float *x_
     a.sf_ts = sf_token_stride;
     a.sf_hs = sf_hidden_stride;
     a.nsf = static_cast<int32_t>(nsf);
+    // token-major rows padded to whole 128-byte lines are written whole
+    const bool whole_lines = sf_hidden_stride == 1 && sf_token_stride > nsf && sf_token_stride % 32 == 0 &&
+                             sf_token_stride - nsf < 32;
+    a.sf_row = static_cast<int32_t>(whole_lines ? sf_token_stride : nsf);
     *out = a;
     return EP_OK;
 }

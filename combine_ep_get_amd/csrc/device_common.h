@@ -105,13 +105,19 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
     }
     if (kMetaLast && meta_lane) write_meta();
     // per-row scale factors, one thread per block of channels, after the
-    // rows so that their loads do not hold the rows' stores back
+    // rows so that their loads do not hold the rows' stores back.  Padded
+    // rows are written whole (sf_row entries, the padding as 0): a line that
+    // neighbouring slots' workgroups, on other XCDs, each write in part cost
+    // the 16384-token FP8 dispatch 242 µs against 225 µs with whole lines
+    // (217 µs without scales).
     if (meta && a.x_sf) {
-        for (int b = threadIdx.x; b < a.nsf; b += NT) {
-            const float v = a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
+        for (int b = threadIdx.x; b < a.sf_row; b += NT) {
+            const bool pad = b >= a.nsf;
+            const float v = pad ? 0.0f : a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
             for (int j = 0; j < c.K; ++j) {
                 const int32_t s = slot_of(lane_slot, j);
-                if (slot_ok(s, c.num_rows)) a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
+                if (slot_ok(s, c.num_rows) && !(pad && s == c.num_rows - 1))
+                    a.recv_sf[s * a.sf_ts + b * a.sf_hs] = v;
             }
         }
     }

@@ -77,6 +77,9 @@ struct CopyParams {
 // Pointers of one dispatch.  Rows are moved as 16-byte vectors whatever
 // their element type; x_sf / recv_sf are the optional per-row scale factors
 // (nsf per row; element (row, b) of recv_sf at row * sf_ts + b * sf_hs).
+// sf_row entries are written per received row: nsf, or the whole padded row
+// (its entries past nsf as 0) when the rows are padded to whole 128-byte
+// lines; the last row of recv_sf never takes the padding.
 struct DispatchArgs {
     const void *x;
     const float *w;
@@ -87,7 +90,7 @@ struct DispatchArgs {
     const float *x_sf;
     float *recv_sf;
     int64_t sf_ts, sf_hs;
-    int32_t nsf;
+    int32_t nsf, sf_row;
 };
 
 constexpr int kCopyThreads = 128;      // dispatch workgroup size

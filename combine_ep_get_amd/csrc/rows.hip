@@ -191,7 +191,15 @@ __global__ __launch_bounds__(kNarrowThreads) void dispatch_narrow_kernel(CopyPar
         if (a.recv_src) a.recv_src[s] = t;
         if (a.recv_w) a.recv_w[s] = a.w ? a.w[e] : 1.0f;
     }
-    if (a.x_sf && v < a.nsf) a.recv_sf[s * a.sf_ts + v * a.sf_hs] = a.x_sf[static_cast<int64_t>(t) * a.nsf + v];
+    if (a.x_sf) {
+        // nsf <= nvec, so entry b < nsf is thread v = b's; the padding of a
+        // padded row (b >= nsf) takes further rounds
+        for (int b = v; b < a.sf_row; b += c.nvec) {
+            const bool pad = b >= a.nsf;
+            if (!(pad && s == c.num_rows - 1))
+                a.recv_sf[s * a.sf_ts + b * a.sf_hs] = pad ? 0.0f : a.x_sf[static_cast<int64_t>(t) * a.nsf + b];
+        }
+    }
 }
 
 template <int KG>

@@ -264,6 +264,12 @@ int ep_quantize_fp8(const ep_problem *problem, const uint16_t *x, uint8_t *x_fp8
  * is (1, R*S rounded up to the alignment).  recv_sf must hold
  * (R*S-1)*sf_token_stride + (H/128-1)*sf_hidden_stride + 1 floats.
  * Requires H % 128 == 0 and strides >= 1.
+ * Token-major rows padded to whole 128-byte lines (sf_hidden_stride 1,
+ * sf_token_stride = H/128 rounded up to a multiple of 32, larger than H/128)
+ * are written whole: entries H/128 .. sf_token_stride-1 of every received
+ * row except the last row of recv_sf (R*S-1) are set to 0.  With recv_sf
+ * 128-byte aligned, no line of the scales is then written in parts by
+ * different workgroups, which is the faster layout for large batches.
  *
  *   x_fp8        [T,H] uint8 device, 16-byte aligned
  *   x_sf         [T,H/128] fp32 device, token-major

@@ -255,3 +255,77 @@ def test_layout_dispatch_fp8_few_chunks(ep, T, K, column_major):
     assert_same(g_sf.cpu().numpy()[sel], rsf[sel])
     assert_same(g_src.cpu().numpy()[s], rsrc[s])
     assert_same(g_w.cpu().numpy()[s], rw[s])
+
+
+def _padded_case(kind):
+    """Routing for the padded-scale-row cases: (idx, w, x, E, R, S)."""
+    rng = np.random.default_rng(len(kind))
+    if kind == "last_row":
+        # two ranks of two experts, one entry on each rank per token: both
+        # slices fill to exactly S = T rows, so row R*S-1 is written
+        T, E, R, H = 300, 4, 2, 1024
+        idx = np.stack([rng.integers(0, 2, T), rng.integers(2, 4, T)], axis=1).astype(np.int32)
+        S = T
+    else:
+        T, K, H = {"two_call": (600, 8, 7168), "single_kernel": (128, 8, 7168),
+                   "chunks": (2000, 8, 7168), "narrow": (3000, 6, 512)}[kind]
+        E, R = 64, 8
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+        idx[rng.random(idx.shape) < 0.03] = -1
+        counts = np.bincount(idx[idx >= 0].ravel(), minlength=E)
+        S = int(counts.reshape(R, -1).sum(1).max()) + 5
+    w = rng.standard_normal(idx.shape).astype(np.float32)
+    x = ep_inputs.bf16_normal(rng, (idx.shape[0], H))
+    return idx, w, x, E, R, S
+
+
+@pytest.mark.parametrize("kind", ["two_call", "single_kernel", "chunks", "narrow", "last_row"])
+def test_dispatch_fp8_scale_rows_padded_to_lines(ep, kind):
+    """Token-major scale rows padded to whole 128-byte lines (token stride
+    H/128 rounded up to 32 floats): the scales bit for bit at the packed
+    layout's values, the padding of every written row 0 except on the last
+    row of the buffer, and nothing written outside the written rows or past
+    the buffer's required size."""
+    print(f"[parity-fp8] padded scale rows {kind}", flush=True)
+    idx, w, x, E, R, S = _padded_case(kind)
+    T, K = idx.shape
+    H = x.shape[1]
+    nb = H // 128
+    pad = -(-nb // 32) * 32
+    assert pad > nb
+    rows = R * S
+    lay = oracle.layout(idx, E, R, S, 1)
+    q, sf = oracle.quantize_fp8(x)
+    rq, rsf, (ts, hs), rsrc, rw = oracle.dispatch_fp8(q, sf, lay.token_slot, rows, w)
+    assert (ts, hs) == (nb, 1)
+    p = ep.Problem.make(T, H, E, K, R, 1, 1, S)
+    bufs = ep.alloc_layout(p)
+    need = (rows - 1) * pad + nb   # the size the interface requires
+    g_q = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+    g_sf = torch.full((rows * pad + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    g_src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(rows, dtype=torch.float32, device="cuda")
+    if kind in ("two_call", "narrow"):   # 512-byte rows take the narrow-row dispatch
+        ep.ep_get_layout(p, dev(idx), *bufs.args())
+        ep.ep_dispatch_fp8(p, dev(q), dev(sf), dev(w), bufs.token_slot, g_q, g_sf, pad, 1, g_src, g_w)
+    else:
+        ep.ep_layout_dispatch_fp8(p, dev(idx), *bufs.args(), None, dev(q), dev(sf), dev(w), g_q, g_sf,
+                                  pad, 1, g_src, g_w)
+    assert ep.ep_read_status(bufs.workspace) == ep.EP_OK
+    assert_same(bufs.token_slot.cpu().numpy(), lay.token_slot, "token_slot")
+    s = lay.token_slot.ravel()
+    s = np.sort(s[s >= 0])
+    assert_same(g_q.cpu().numpy()[s], rq[s])
+    assert_same(g_src.cpu().numpy()[s], rsrc[s])
+    assert_same(g_w.cpu().numpy()[s], rw[s])
+    got = g_sf.cpu().numpy()
+    grid = got[:rows * pad].reshape(rows, pad)
+    assert_same(grid[s, :nb], rsf.reshape(rows, nb)[s])
+    inner = s[s != rows - 1]
+    assert np.all(grid[inner, nb:].view(np.uint32) == 0), "padding of written rows"
+    unwritten = np.setdiff1d(np.arange(rows), s)
+    assert np.all(np.isnan(grid[unwritten])), "rows no slot names"
+    assert np.all(np.isnan(got[need:])), "past the required size"
+    if kind == "last_row":
+        assert s[-1] == rows - 1
+        assert np.all(np.isnan(grid[rows - 1, nb:]))
