@@ -17,6 +17,10 @@ HIPCC_FLAGS = [
     "-Wall", "-Werror=return-type",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the leading scalar kernel arguments (up to 14 dwords) arrive in SGPRs,
+    # not through a load at the start of every wave: the decode-sized
+    # kernels take their first loads' operands that way
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -813,9 +813,20 @@ __device__ void fused_layout(const LayoutParams &p, int *lds) {
 // workgroups have the linear ids, and so the XCDs, that dispatch_kernel
 // gives them, which the combine's grid shares: rows a small batch leaves in
 // an XCD's L2 are read back there.
+// The operands of a dispatching workgroup's first loads (the ids, the row,
+// the batch sizes) also come as leading scalar arguments, which arrive
+// preloaded in SGPRs; the structures' other fields load while those loads
+// are in flight.
 template <int VPT, int kMaxEntries>
-__global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(LayoutParams p, CopyParams c,
-                                                                       DispatchArgs a) {
+__global__ __launch_bounds__(kFusedThreads) void layout_dispatch_kernel(
+    const int32_t *topk_idx, const void *x, int32_t T, int32_t K, int32_t E, int32_t nvec, LayoutParams p,
+    CopyParams c, DispatchArgs a) {
+    p.topk_idx = topk_idx;
+    p.T = c.T = T;
+    p.K = c.K = K;
+    p.E = E;
+    c.nvec = nvec;
+    a.x = x;
     extern __shared__ __align__(16) int smem[];
     __shared__ int s_wsum[2 * kFusedThreads / 64];
     if (blockIdx.y == 0) {
@@ -1141,9 +1152,11 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
 #define EP_LAYOUT_DISPATCH_CASE(V)                                                                   \
     case V:                                                                                          \
         if (p.nchunks == 1)                                                                          \
-            layout_dispatch_kernel<V, kChunkEntries><<<grid, kFusedThreads, lds, stream>>>(p, cp, a); \
+            layout_dispatch_kernel<V, kChunkEntries><<<grid, kFusedThreads, lds, stream>>>(         \
+                p.topk_idx, a.x, p.T, p.K, p.E, cp.nvec, p, cp, a);                                 \
         else                                                                                         \
-            layout_dispatch_kernel<V, kFusedMaxEntries><<<grid, kFusedThreads, lds, stream>>>(p, cp, a); \
+            layout_dispatch_kernel<V, kFusedMaxEntries><<<grid, kFusedThreads, lds, stream>>>(      \
+                p.topk_idx, a.x, p.T, p.K, p.E, cp.nvec, p, cp, a);                                 \
         break;
         EP_LAYOUT_DISPATCH_CASE(1)
         EP_LAYOUT_DISPATCH_CASE(2)
