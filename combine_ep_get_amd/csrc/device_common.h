@@ -106,10 +106,10 @@ __device__ __forceinline__ void store_token_rows(const CopyParams &c, const Disp
     if (kMetaLast && meta_lane) write_meta();
     // per-row scale factors, one thread per block of channels, after the
     // rows so that their loads do not hold the rows' stores back.  Padded
-    // rows are written whole (sf_row entries, the padding as 0): a line that
-    // neighbouring slots' workgroups, on other XCDs, each write in part cost
-    // the 16384-token FP8 dispatch 242 µs against 225 µs with whole lines
-    // (217 µs without scales).
+    // rows are written whole (sf_row entries, the padding as 0).  A line
+    // shared by neighbouring slots, whose workgroups on different XCDs each
+    // write part of it, made the 16384-token FP8 dispatch take 242 µs; with
+    // whole lines it takes 225 µs (217 µs without scales).
     if (meta && a.x_sf) {
         for (int b = threadIdx.x; b < a.sf_row; b += NT) {
             const bool pad = b >= a.nsf;

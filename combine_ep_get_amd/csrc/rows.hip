@@ -143,8 +143,8 @@ struct KeepAll {
 // Its arguments are scalars only, all within the 14 dwords that arrive
 // preloaded in SGPRs, and the workgroup width is one of them (blockDim
 // would be a load of its own): no wave waits for a kernel-argument load
-// before its first loads, which took 0.2-0.3 µs off the combine of a
-// 128- or 256-token batch.
+// before its first loads, which took about 0.2-0.3 µs off the 128- and
+// 256-token steps.
 template <int KG>
 __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     const uint16_t *__restrict__ y, const int32_t *__restrict__ slot, const float *__restrict__ w,
