@@ -366,30 +366,45 @@ __device__ __forceinline__ void wave_assign_slots(const LayoutParams &p, int64_t
 
 constexpr int kCountEPT = (EP_MAX_EXPERTS + kCountThreads - 1) / kCountThreads;
 
-// Multi-chunk pass 1: one workgroup per chunk writes its histogram row.  For
-// the one-call layout and dispatch (p.count_t set) it also writes, expert-
-// major, the chunk's count of each expert and the chunk's count of the lower
-// experts of the same rank (an exclusive scan of the histogram restarted at
-// each rank's first expert).
+// Multi-chunk pass 1: the chunk's histogram row.  For the one-call layout
+// and dispatch (p.count_t set) it also writes, expert-major, the chunk's
+// count of each expert and the chunk's count of the lower experts of the
+// same rank (an exclusive scan of the histogram restarted at each rank's
+// first expert); there each chunk has two workgroups side by side, so that
+// the token pass (the rank map and unique tokens) no longer precedes the
+// expert counts the next launch waits for: workgroups [0, nchunks) count
+// experts and bad ids, [nchunks, 2 nchunks) map tokens, each writing its
+// own columns of the row (1024-8192 tokens: the layout-and-dispatch phase
+// 0.75-1.1 µs shorter).  Otherwise one workgroup per chunk does both.
 // LDS: s_idx [kChunkEntries] | s_hist [pitch] | s_raw [E+1] | s_aln [E+1].
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(LayoutParams p) {
     extern __shared__ __align__(16) int smem[];
     __shared__ int s_wsum[2 * kCountThreads / 64];
     int *s_idx = smem;
     int *s_hist = smem + kChunkEntries;
-    const int c = blockIdx.x;
+    const bool split = p.count_t != nullptr;
+    const int c = split ? static_cast<int>(blockIdx.x) % p.nchunks : blockIdx.x;
+    const bool experts = !split || static_cast<int>(blockIdx.x) < p.nchunks;
+    const bool tokens = !split || static_cast<int>(blockIdx.x) >= p.nchunks;
     const int t0 = c * p.chunk_tokens, t1 = min(p.T, t0 + p.chunk_tokens);
     const int n = (t1 - t0) * p.K;
     load_ids<kCountThreads>(p.topk_idx + static_cast<int64_t>(t0) * p.K, n, s_idx);
     for (int i = threadIdx.x; i < p.ncols; i += kCountThreads) s_hist[i] = 0;
     __syncthreads();
-    entry_pass<kCountThreads>(p, n, 1, s_idx, s_hist, nullptr);
+    // packs every entry (rank next to id); counts experts only in the expert role
+    entry_pass<kCountThreads>(p, n, 1, s_idx, experts ? s_hist : nullptr, nullptr);
     __syncthreads();
-    token_pass<kCountThreads>(p, t0, t1, s_idx, s_hist);
-    __syncthreads();
+    if (tokens) {
+        token_pass<kCountThreads>(p, t0, t1, s_idx, s_hist);
+        __syncthreads();
+    }
     int32_t *row = p.table + static_cast<int64_t>(c) * p.pitch;
-    for (int i = threadIdx.x; i < p.ncols; i += kCountThreads) row[i] = s_hist[i];
-    if (p.count_t) {
+    const int bad_col = p.E + p.R + p.G;
+    for (int i = threadIdx.x; i < p.ncols; i += kCountThreads) {
+        const bool expert_col = i < p.E || i == bad_col;
+        if (expert_col ? experts : tokens) row[i] = s_hist[i];
+    }
+    if (split && experts) {
         int *s_raw = s_hist + p.pitch;
         int *s_aln = s_raw + (p.E + 1);
         block_scan_counts<kCountThreads, kCountEPT>(p, s_hist, s_aln, s_raw, s_wsum);
@@ -1111,7 +1126,8 @@ hipError_t launch_layout_dispatch(const LayoutParams &p, const CopyParams &c, co
         // finishes the layout and dispatches, each workgroup deriving its
         // token's slots
         const size_t lds_count = sizeof(int) * (kChunkEntries + p.pitch + 2 * (p.E + 1));
-        layout_count_kernel<<<p.nchunks, kCountThreads, lds_count, stream>>>(p);
+        // two workgroups per chunk: expert counts and the token pass side by side
+        layout_count_kernel<<<2 * p.nchunks, kCountThreads, lds_count, stream>>>(p);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         const size_t lds = sizeof(int) * 2 * (p.E + 1);
