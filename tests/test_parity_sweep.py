@@ -1,6 +1,8 @@
 """A seeded sweep of random problems through the one-call layout and
 dispatch against the CPU oracle: every layout output, slot, received row,
-source index and weight bit for bit, rows no slot names left untouched.
+source index and weight bit for bit, rows no slot names left untouched; then
+the combine of expert outputs in that layout, weighted and with unit
+weights, within the combine tolerance.
 
 The draws span the interface: R from 1 to 256 ranks, 1 to 64 experts per
 rank, top-k 1 to 32, batches from one token to 20000 (one chunk, two to four,
@@ -8,10 +10,11 @@ up to 128 and beyond, so every layout form runs), groups, alignment 1, 2 and
 4, empty entries, duplicate experts, bad ids, and slices sized to overflow."""
 import numpy as np
 import pytest
+import torch
 
 import ep_inputs
 import oracle
-from test_parity import tight_stride
+from test_parity import bf16_dev, combine_close, dev, host_u16, tight_stride
 from test_parity_fused import ep, run_fused  # noqa: F401  (ep is a fixture)
 
 pytestmark = pytest.mark.gpu
@@ -54,4 +57,20 @@ def draw(seed, big):
 @pytest.mark.parametrize("seed,big", [(s, False) for s in range(60)] + [(1000 + s, True) for s in range(30)])
 def test_random_problem(ep, seed, big):
     idx, w, x, E, R, G, A, S = draw(seed, big)
-    run_fused(ep, idx, w, x, E, R, G, A=A, S=S, cumulative=seed % 5 == 0)
+    ref, bufs = run_fused(ep, idx, w, x, E, R, G, A=A, S=S, cumulative=seed % 5 == 0)
+    T, K = idx.shape
+    H = x.shape[1]
+    if T == 0:
+        return
+    rows = R * S
+    ref_rx, _, _ = oracle.dispatch(x, ref.token_slot, rows, w)
+    y = ep_inputs.permuted_rows(ref_rx, seed=seed)
+    p = ep.Problem.make(T, H, E, K, R, G, A, S)
+    d_y = bf16_dev(y)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    out_unit = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(p, d_y, bufs.token_slot, dev(w), out)
+    ep.ep_combine(p, d_y, bufs.token_slot, None, out_unit)
+    torch.cuda.synchronize()
+    combine_close(host_u16(out), oracle.combine(y, ref.token_slot, w))
+    combine_close(host_u16(out_unit), oracle.combine(y, ref.token_slot, None))
